@@ -1,0 +1,199 @@
+"""Seeded synthetic inputs for the attention forward workloads.
+
+This module is the only code shared by the GPU path's tests and the CPU oracle:
+it draws random numbers and rounds them to the storage dtype, and holds none of
+the attention arithmetic.
+
+Recipe (one ``numpy.random.Generator(PCG64(seed))`` per tensor, seed =
+1000 * config_id + t with t = 0 for Q, 1 for K, 2 for V, 3 for the choice of
+peaked key rows):
+
+* values are float32 ``standard_normal`` draws in the *storage order* of the
+  workload's layout (BHND = [B,H,N,d], BSND = [B,N,H,d]), times the tensor's
+  standard deviation;
+* in the long-context workload, round(1% of Nk) distinct key positions per
+  (b, h) are drawn and those K rows multiplied by 8 (exact in binary floating
+  point, so the order against rounding does not matter);
+* bf16 workloads then round every value to bf16, round-to-nearest-even.  The
+  GPU receives the bf16 bits; the oracle receives the same values widened to
+  float32 (exact).
+
+The shapes are those of the pages' workloads: an LLaMA-13B-like prefill
+(32 heads of 128, [pwwt] "measured performance"), the B=4 H=32 D=128
+self-attention of [ascendai] section 4.3, a Stable-Diffusion-style
+cross-attention ([ascendai] section 4.2: 128x128 latent tokens against a
+77-token context), and a 128K causal context ([ascendai] sections 1.3 and 4.3).
+Trained weights do not exist here: N(0, sigma^2) activations of those shapes
+stand in for the models' activations.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    cid: int            # config id, used in the seeds
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str          # "bf16" or "f32"
+    layout: str         # "BHND" or "BSND"
+    causal: bool
+    sigma_q: float = 1.0
+    sigma_k: float = 1.0
+    sigma_v: float = 1.0
+    peaked_frac: float = 0.0   # fraction of K rows scaled by peaked_mult
+    peaked_mult: float = 8.0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def flops(self) -> float:
+        """4*B*H*Nq*Nk*d, halved for causal (the dense count, not N(N+1)/2)."""
+        f = 4.0 * self.B * self.H * self.Nq * self.Nk * self.d
+        return f / 2 if self.causal else f
+
+    def q_shape(self):
+        return self._shape(self.Nq)
+
+    def kv_shape(self):
+        return self._shape(self.Nk)
+
+    def _shape(self, n):
+        if self.layout == "BHND":
+            return (self.B, self.H, n, self.d)
+        return (self.B, n, self.H, self.d)
+
+    def scaled(self, **changes) -> "Workload":
+        return dataclasses.replace(self, **changes)
+
+
+WORKLOADS = {
+    "tiny_f32": Workload(1, "tiny_f32", 1, 2, 256, 256, 64, "f32", "BHND", False),
+    "llama_prefill_causal": Workload(2, "llama_prefill_causal", 1, 32, 4096, 4096, 128,
+                                     "bf16", "BSND", True),
+    "selfattn_b4h32n8k": Workload(3, "selfattn_b4h32n8k", 4, 32, 8192, 8192, 128,
+                                  "bf16", "BHND", False),
+    "sd_crossattn": Workload(4, "sd_crossattn", 2, 8, 16384, 77, 64, "bf16", "BHND", False,
+                             sigma_k=0.5, sigma_v=0.5),
+    "long_causal_128k": Workload(5, "long_causal_128k", 1, 32, 131072, 131072, 128,
+                                 "bf16", "BSND", True, peaked_frac=0.01),
+}
+BY_ID = {w.cid: w for w in WORKLOADS.values()}
+
+
+# ----------------------------------------------------------------------------
+# bf16 storage conversion (round to nearest, ties to even)
+
+_CHUNK = 1 << 24
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) of float32 values, round-to-nearest-even.
+    Inputs here are finite; NaN handling is not needed."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint16)
+    for a in range(0, flat.size, _CHUNK):
+        u = flat[a:a + _CHUNK].view(np.uint32)
+        bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+        out[a:a + _CHUNK] = ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    return out.reshape(x.shape)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    flat = b.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.float32)
+    ov = out.view(np.uint32)
+    for a in range(0, flat.size, _CHUNK):
+        ov[a:a + _CHUNK] = flat[a:a + _CHUNK].astype(np.uint32) << np.uint32(16)
+    return out.reshape(b.shape)
+
+
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class Inputs:
+    w: Workload
+    q: np.ndarray                 # float32 values (exact input values), storage order
+    k: np.ndarray
+    v: np.ndarray
+    q_bits: np.ndarray | None     # uint16 bf16 bits (bf16 workloads only)
+    k_bits: np.ndarray | None
+    v_bits: np.ndarray | None
+    peaked: np.ndarray | None     # [B, H, n_peaked] key positions scaled up, or None
+
+
+def _draw(seed: int, shape, sigma: float) -> np.ndarray:
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = g.standard_normal(size=shape, dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    return x
+
+
+def peaked_positions(w: Workload, seed_base: int | None = None) -> np.ndarray | None:
+    """Key positions whose K rows are scaled, per (b, h), drawn from seed
+    1000*cid+3 (or seed_base+3)."""
+    if w.peaked_frac <= 0:
+        return None
+    base = 1000 * w.cid if seed_base is None else seed_base
+    n = int(round(w.peaked_frac * w.Nk))
+    g = np.random.Generator(np.random.PCG64(base + 3))
+    pos = np.empty((w.B, w.H, n), dtype=np.int64)
+    for b in range(w.B):
+        for h in range(w.H):
+            pos[b, h] = np.sort(g.choice(w.Nk, size=n, replace=False))
+    return pos
+
+
+def make_inputs(w: Workload, seed_base: int | None = None) -> Inputs:
+    """Inputs of workload ``w``.  ``seed_base`` replaces 1000*cid (for extra
+    cases of the same recipe at other shapes)."""
+    base = 1000 * w.cid if seed_base is None else seed_base
+    q = _draw(base + 0, w.q_shape(), w.sigma_q)
+    k = _draw(base + 1, w.kv_shape(), w.sigma_k)
+    v = _draw(base + 2, w.kv_shape(), w.sigma_v)
+    pos = peaked_positions(w, seed_base)
+    if pos is not None:
+        mult = np.float32(w.peaked_mult)
+        for b in range(w.B):
+            for h in range(w.H):
+                if w.layout == "BHND":
+                    k[b, h, pos[b, h], :] *= mult
+                else:
+                    k[b, pos[b, h], h, :] *= mult
+    if w.dtype == "bf16":
+        qb, kb, vb = f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+        q, k, v = bf16_bits_to_f32(qb), bf16_bits_to_f32(kb), bf16_bits_to_f32(vb)
+        return Inputs(w, q, k, v, qb, kb, vb, pos)
+    if w.dtype != "f32":
+        raise ValueError(f"unknown dtype {w.dtype!r}")
+    return Inputs(w, q, k, v, None, None, None, pos)
+
+
+def sample_rows(w: Workload, n: int, seed: int = 7, peaked: np.ndarray | None = None) -> np.ndarray:
+    """A sorted, de-duplicated sample of query rows for row-sampled checks:
+    the first 16 and last 16 rows, up to 16 rows right after peaked keys of
+    head (0, 0) when there are any, and seeded-uniform rows for the rest."""
+    rows = set(range(min(16, w.Nq)))
+    rows.update(range(max(0, w.Nq - 16), w.Nq))
+    if peaked is not None:
+        for p in peaked[0, 0][:16]:
+            if p + 1 < w.Nq:
+                rows.add(int(p) + 1)
+    g = np.random.Generator(np.random.PCG64(seed))
+    need = max(0, n - len(rows))
+    if need:
+        rows.update(int(x) for x in g.choice(w.Nq, size=min(need, w.Nq), replace=False))
+    return np.array(sorted(rows), dtype=np.int32)

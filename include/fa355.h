@@ -1,0 +1,97 @@
+/*
+ * fa355.h -- C ABI of libfa355, the attention forward pass for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation (pages cited by site: [nanhubrain] = nanhubrain.csdn.net,
+ * FlashAttention in CANN ops-transformer; [pwwt] = www.pwwt.cn/news/2518640;
+ * [ascendai] = ascendai.csdn.net, efficient attention in CANN ops-nn):
+ *
+ *   O = softmax(scale * Q K^T [causal mask]) V            per (batch, head)
+ *   LSE_i = ln sum_{j visible to i} exp(scale * q_i . k_j)
+ *
+ * -- [nanhubrain] "exact source of the quadratic memory" (the three-step
+ * definition), [nanhubrain] "tiling skeleton" and "online softmax mathematics"
+ * (computed block by block with a running row max and row sum, so the N x N
+ * score matrix is never stored), [ascendai] section 3.1 (operator interface:
+ * query/key/value/output, a softmax scale whose negative default means
+ * 1/sqrt(d), a causal flag) and section 6.1 (causal = the strict upper
+ * triangle masked: key j is visible to query i iff j <= i, top-left aligned
+ * when Nq != Nk), [pwwt] "standard vs IO-aware" (the BSND layout option).
+ * The per-row log-sum-exp is the statistic from which [nanhubrain] "backward
+ * recomputation" rebuilds the probabilities: P_ij = exp(scale*q_i.k_j - LSE_i).
+ */
+#ifndef FA355_H
+#define FA355_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad enum, misalignment, NaN/inf scale */
+    FA_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement (e.g. d not 64/128) */
+    FA_ERR_HIP = 3            /* the HIP runtime reported an error at launch */
+} fa_status;
+
+typedef enum fa_layout {
+    FA_BHND = 0,   /* [B, H, N, d]: each head's rows contiguous             */
+    FA_BSND = 1    /* [B, N, H, d]: batch-seq-head-dim, heads interleaved   */
+} fa_layout;
+
+typedef enum fa_dtype {
+    FA_BF16 = 0,   /* bfloat16 */
+    FA_F32 = 1     /* IEEE float32 */
+} fa_dtype;
+
+/*
+ * fa_fwd -- enqueue one attention forward pass on `stream`.
+ *
+ * q        device pointer, Q in `layout` with N = Nq, element type `in_dtype`.
+ * k, v     device pointers, K and V in `layout` with N = Nk, type `in_dtype`.
+ * o        device pointer, O written in Q's layout ([B,H,Nq,d] or [B,Nq,H,d]),
+ *          element type `o_dtype` (FA_F32 or FA_BF16; FA_BF16 only for
+ *          bf16 inputs).
+ * lse      device pointer to float32 [B, H, Nq] (always this order,
+ *          contiguous), natural-log log-sum-exp of each row's scaled scores;
+ *          NULL = not written.
+ * B, H     batch size and number of heads, >= 1.
+ * Nq, Nk   query and key/value sequence lengths, >= 1 (any value: no tile
+ *          multiple is required).
+ * d        head dimension: 64 or 128 (else FA_ERR_UNSUPPORTED).
+ * scale    softmax scale applied to q.k; a negative value selects 1/sqrt(d);
+ *          0 is valid (uniform weights); NaN or infinity is FA_ERR_INVALID_ARG.
+ * causal   0: every key is visible; non-zero: key j visible to query i iff
+ *          j <= i (top-left alignment for any Nq, Nk).
+ * layout   FA_BHND or FA_BSND; all of q, k, v, o are dense (no padding).
+ * in_dtype FA_BF16 or FA_F32 (q, k and v share it).
+ * o_dtype  FA_F32 or FA_BF16.
+ * stream   a hipStream_t (NULL = the null stream).
+ *
+ * Alignment: q, k, v, o must be 16-byte aligned, lse 4-byte aligned.  o and
+ * lse must not overlap q, k, v or each other.
+ *
+ * Ownership and asynchrony: the caller allocates and owns every buffer; the
+ * library allocates no device memory and keeps no per-call state.  The call
+ * validates its arguments, launches one kernel on `stream` and returns without
+ * synchronising; buffers must stay valid until the stream reaches the kernel's
+ * end.  Validation failures return before any HIP call.  Results are
+ * deterministic: a fixed reduction order, no atomics.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                 int layout, int in_dtype, int o_dtype, void* stream);
+
+/* A static, human-readable name for a status code (never NULL). */
+const char* fa_status_str(int status);
+
+/* ABI version of this header (incremented on incompatible change). */
+int fa_abi_version(void);
+
+#define FA355_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA355_H */

@@ -1,0 +1,149 @@
+"""CPU oracle for the attention forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never calls it, and
+it shares no code with the GPU path (the only common module is the seeded
+input generator, which holds none of the method's arithmetic).
+
+Two implementations live here:
+
+* ``attn_fwd`` -- the plain definition, a two-pass fp64 softmax attention in C
+  (``oracle.c``): scores, row max, exp-sum, weighted sum of values, one row at
+  a time.  It follows [nanhubrain] "exact source of the quadratic memory"
+  (S = QK^T/sqrt(d), P = softmax(S), O = PV), [nanhubrain] "online softmax
+  mathematics" (max-subtracted softmax) and [ascendai] section 6.1 (causal:
+  strict upper triangle masked, key j visible to query i iff j <= i).
+* ``online.attn_fwd_online`` -- the pages' own algorithm, the tiled forward
+  with the online-softmax recurrence ([nanhubrain] "tiling skeleton",
+  [ascendai] section 2.2), in numpy fp64, over caller-chosen block splits.
+
+Page key: [nanhubrain] = nanhubrain.csdn.net (FlashAttention in CANN
+ops-transformer), [pwwt] = www.pwwt.cn/news/2518640, [ascendai] =
+ascendai.csdn.net (efficient attention in CANN ops-nn).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "oracle.c")
+LIBRARY = os.path.join(_HERE, "liboracle.so")
+
+_c_i64 = ctypes.c_int64
+_c_int = ctypes.c_int
+_c_dbl = ctypes.c_double
+_c_ptr = ctypes.c_void_p
+
+
+def build(source: str = SOURCE, output: str = LIBRARY) -> str:
+    """Compile ``oracle.c`` with gcc (plain -O2, no fast-math) into a shared library."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-Wall", "-Wextra", "-o", output, source, "-lm"]
+    subprocess.run(cmd, check=True)
+    return output
+
+
+class OracleLib:
+    """ctypes view of one compiled oracle library (the default, or a test variant)."""
+
+    def __init__(self, path: str = LIBRARY):
+        if not os.path.exists(path):
+            raise FileNotFoundError(
+                f"oracle library {path} is not built; run oracle.build() first")
+        self.path = path
+        self._lib = ctypes.CDLL(path)
+        f = self._lib.oracle_attn_fwd
+        f.restype = _c_int
+        f.argtypes = ([_c_ptr] * 3 + [_c_i64] * 9 + [_c_int] * 5 + [_c_dbl, _c_int]
+                      + [_c_ptr, _c_int, _c_ptr, _c_ptr, _c_int])
+        g = self._lib.oracle_attn_probs
+        g.restype = _c_int
+        g.argtypes = [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_int, _c_int, _c_int,
+                      _c_dbl, _c_int, _c_ptr]
+        self._lib.oracle_max_threads.restype = _c_int
+
+    def max_threads(self) -> int:
+        return int(self._lib.oracle_max_threads())
+
+    def attn_fwd(self, q, k, v, *, scale: float, causal: bool = False,
+                 layout: str = "BHND", rows=None, n_threads: int = 0):
+        """O [B,H,R,d] and LSE [B,H,R] in float64.
+
+        q, k, v: float32 arrays in the layout's storage shape -- ``BHND`` is
+        [B,H,N,d], ``BSND`` is [B,N,H,d].  ``rows``: optional query indices
+        (the same for every (b,h)); default all rows.  ``scale`` is used as
+        given (no default resolution here).
+        """
+        q = np.ascontiguousarray(q, dtype=np.float32)
+        k = np.ascontiguousarray(k, dtype=np.float32)
+        v = np.ascontiguousarray(v, dtype=np.float32)
+        if layout == "BHND":
+            B, H, Nq, d = q.shape
+            Nk = k.shape[2]
+            qs = (H * Nq * d, Nq * d, d)
+            ks = (H * Nk * d, Nk * d, d)
+        elif layout == "BSND":
+            B, Nq, H, d = q.shape
+            Nk = k.shape[1]
+            qs = (Nq * H * d, d, H * d)
+            ks = (Nk * H * d, d, H * d)
+        else:
+            raise ValueError(f"unknown layout {layout!r}")
+        if k.shape != v.shape:
+            raise ValueError("k and v must have the same shape")
+        if rows is None:
+            R = Nq
+            rows_arr = None
+            rows_ptr = None
+        else:
+            rows_arr = np.ascontiguousarray(rows, dtype=np.int32)
+            R = int(rows_arr.size)
+            rows_ptr = rows_arr.ctypes.data
+        o = np.empty((B, H, R, d), dtype=np.float64)
+        lse = np.empty((B, H, R), dtype=np.float64)
+        rc = self._lib.oracle_attn_fwd(
+            q.ctypes.data, k.ctypes.data, v.ctypes.data,
+            *qs, *ks, *ks, B, H, Nq, Nk, d, float(scale), int(bool(causal)),
+            rows_ptr, R, o.ctypes.data, lse.ctypes.data, int(n_threads))
+        if rc != 0:
+            raise RuntimeError(f"oracle_attn_fwd failed with code {rc}")
+        return o, lse
+
+    def attn_probs(self, q, k, *, scale: float, causal: bool = False):
+        """P [Nq, Nk] (float64) of one head; q [Nq,d], k [Nk,d] float32."""
+        q = np.ascontiguousarray(q, dtype=np.float32)
+        k = np.ascontiguousarray(k, dtype=np.float32)
+        Nq, d = q.shape
+        Nk = k.shape[0]
+        p = np.empty((Nq, Nk), dtype=np.float64)
+        rc = self._lib.oracle_attn_probs(q.ctypes.data, k.ctypes.data, d, d,
+                                         Nq, Nk, d, float(scale), int(bool(causal)),
+                                         p.ctypes.data)
+        if rc != 0:
+            raise RuntimeError(f"oracle_attn_probs failed with code {rc}")
+        return p
+
+
+_default: OracleLib | None = None
+
+
+def lib() -> OracleLib:
+    """The default oracle library, built on first use if it is missing."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIBRARY):
+            build()
+        _default = OracleLib(LIBRARY)
+    return _default
+
+
+def attn_fwd(q, k, v, **kw):
+    return lib().attn_fwd(q, k, v, **kw)
+
+
+def attn_probs(q, k, **kw):
+    return lib().attn_probs(q, k, **kw)
