@@ -1,0 +1,208 @@
+"""Benchmark of the attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one call of the HIP forward kernel (the whole hot path: Q tile
+load, K/V staging, S = Q K^T, mask, online softmax, P V, epilogue) over the
+workload's batch, inputs resident in HBM.  Prints one JSON line with the
+throughput in TFLOP/s (4*B*H*Nq*Nk*d, halved for causal) and:
+
+* roofline: the kernel's achieved TFLOP/s against MI355X's dense bf16 MFMA peak
+  (2.5 PFLOP/s), timed live with HIP events on the stream the kernel runs on;
+  ``traffic`` is the HBM bytes per launch from the committed rocprofv3 counter
+  summary, or null when the kernel source changed since it was taken;
+* cpu_baseline: the fp64 CPU oracle timed on this host's cores on a bounded
+  sample of the same workload (rows of the first heads, about 10 s of work),
+  as a reported baseline, not a target.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOPS and % of bf16 MFMA peak at B4 H32 N8192 d128"
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA (published)
+PEAK_F32_TFLOPS = 157.3            # MI355X fp32 (matrix and vector), published
+PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
+
+
+def algorithmic_bytes(w, out_bytes: int) -> float:
+    """Read Q, K, V once, write O and LSE once (per launch)."""
+    el = 2 if w.dtype == "bf16" else 4
+    per_head = (w.Nq + 2 * w.Nk) * w.d * el + w.Nq * w.d * out_bytes + w.Nq * 4
+    return float(per_head) * w.B * w.H
+
+
+KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_112_amd", "csrc", "fa_fwd.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch from profiles/<...>_counters.md, if the summary was
+    taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"fa_fwd_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, inp, target_s: float = 10.0):
+    """Time the fp64 oracle on rows 0, 4, 8, ... of consecutive heads until at
+    least ``target_s`` seconds of work are done (bounded by the workload)."""
+    import numpy as np
+    import oracle
+
+    lib = oracle.lib()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or lib.max_threads()
+    rows = np.arange(0, w.Nq, 4, dtype=np.int32)
+    heads_per_chunk = 2
+    done_heads, flops, elapsed = 0, 0.0, 0.0
+    total_heads = w.B * w.H
+    while done_heads < total_heads and elapsed < target_s:
+        n = min(heads_per_chunk, total_heads - done_heads)
+        sl = []
+        for t in range(done_heads, done_heads + n):
+            b, h = divmod(t, w.H)
+            if w.layout == "BHND":
+                sl.append((inp.q[b:b + 1, h:h + 1], inp.k[b:b + 1, h:h + 1], inp.v[b:b + 1, h:h + 1]))
+            else:
+                sl.append((inp.q[b:b + 1, :, h:h + 1], inp.k[b:b + 1, :, h:h + 1], inp.v[b:b + 1, :, h:h + 1]))
+        t0 = time.perf_counter()
+        for q, k, v in sl:
+            lib.attn_fwd(q, k, v, scale=w.scale, causal=w.causal, layout=w.layout, rows=rows,
+                         n_threads=threads)
+        elapsed += time.perf_counter() - t0
+        if w.causal:
+            per_head = float(sum(4.0 * min(int(r) + 1, w.Nk) * w.d for r in rows))
+        else:
+            per_head = 4.0 * len(rows) * w.Nk * w.d
+        flops += n * per_head
+        done_heads += n
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fp64 two-pass oracle on every 4th query row ({len(rows)} rows) of the first "
+                   f"{done_heads} of {total_heads} heads of {w.name}; {flops:.3e} flop in "
+                   f"{elapsed:.1f} s on {threads} threads"),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="selfattn_b4h32n8k")
+    ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (for profiler runs)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path would shard by heads, see the design notes)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import exact_attention_112_amd as fa
+    from exact_attention_112_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU", file=sys.stderr)
+        return 1
+    w = I.WORKLOADS[args.workload]
+    fa.load()
+    print(f"bench: generating inputs for {w.name}", file=sys.stderr, flush=True)
+    inp = I.make_inputs(w)
+    if w.dtype == "bf16":
+        up = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda")
+        tq, tk, tv = up(inp.q_bits), up(inp.k_bits), up(inp.v_bits)
+    else:
+        tq, tk, tv = (torch.from_numpy(x).to("cuda") for x in (inp.q, inp.k, inp.v))
+    out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
+    o = torch.empty(tq.shape, dtype=out_dtype, device="cuda")
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+
+    def step():
+        fa.fwd(tq, tk, tv, causal=w.causal, scale=w.scale, layout=w.layout, out_dtype=out_dtype,
+               out=o, lse=lse)
+
+    print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    print(f"bench: timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    if not (torch.isfinite(o).all() and torch.isfinite(lse).all()):
+        print("bench: non-finite output", file=sys.stderr)
+        return 1
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, inp)
+
+    traffic = traffic_from_profiles(w.name)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    nbytes = algorithmic_bytes(w, 2 if args.out_dtype == "bf16" else 4)
+    if w.flops / nbytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        gbs = nbytes / (ms * 1e-3) / 1e9     # below the ridge point: HBM-bound
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tflops / peak, 4), "traffic": traffic}
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) Q/K/V of the workload's shape)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "layout": w.layout, "out_dtype": args.out_dtype},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

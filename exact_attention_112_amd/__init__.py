@@ -1,0 +1,146 @@
+"""libfa355: attention forward pass on AMD Instinct MI355X (gfx950).
+
+Python binding of the C ABI in ``include/fa355.h``: argument marshalling only.
+Every step of the computation runs in the HIP kernels of ``libfa355.so``;
+PyTorch is used for device memory and streams.  There is no CPU fallback:
+if the library is not built, or no GPU is present, calls raise.
+
+    O, LSE = fwd(q, k, v, causal=False, scale=None, layout="BHND",
+                 out_dtype=torch.float32)
+
+computes O = softmax(scale * Q K^T [causal]) V per (batch, head) and the
+per-row natural-log log-sum-exp (pages: [nanhubrain] = nanhubrain.csdn.net
+"exact source of the quadratic memory", "tiling skeleton", "online softmax
+mathematics"; [ascendai] = ascendai.csdn.net sections 3.1 and 6.1).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libfa355.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_BHND, FA_BSND = 0, 1
+FA_BF16, FA_F32 = 0, 1
+LAYOUTS = {"BHND": FA_BHND, "BSND": FA_BSND}
+
+# the symbols include/fa355.h declares
+EXPORTS = ("fa_fwd", "fa_status_str", "fa_abi_version")
+ABI_VERSION = 1
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A non-OK fa_status from the library."""
+
+    def __init__(self, status: int, msg: str = ""):
+        self.status = status
+        super().__init__(f"{fa_status_str(status)}{': ' + msg if msg else ''}")
+
+
+class FaInvalidArgument(FaError, ValueError):
+    pass
+
+
+class FaUnsupported(FaError, NotImplementedError):
+    pass
+
+
+def load(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load libfa355.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it first (python -m exact_attention_112_amd.build "
+            "or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(path)
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_float]
+                           + [ctypes.c_int] * 4 + [ctypes.c_void_p])
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_status_str.argtypes = [ctypes.c_int]
+    lib.fa_abi_version.restype = ctypes.c_int
+    lib.fa_abi_version.argtypes = []
+    if lib.fa_abi_version() != ABI_VERSION:
+        raise ImportError(f"libfa355 ABI {lib.fa_abi_version()} != binding ABI {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def fa_status_str(status: int) -> str:
+    return load().fa_status_str(int(status)).decode()
+
+
+def fa_fwd(q: int, k: int, v: int, o: int, lse: int | None, B: int, H: int, Nq: int, Nk: int,
+           d: int, scale: float, causal: int, layout: int, in_dtype: int, o_dtype: int,
+           stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the fa_status."""
+    return int(load().fa_fwd(q, k, v, o, lse or None, B, H, Nq, Nk, d, float(scale),
+                             int(causal), int(layout), int(in_dtype), int(o_dtype), stream or None))
+
+
+def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, layout: str = "BHND",
+        out_dtype=None, out=None, lse=None, return_lse: bool = True):
+    """Attention forward on torch CUDA tensors (ROCm).
+
+    q: [B,H,Nq,d] (BHND) or [B,Nq,H,d] (BSND); k, v: same with Nk.  bf16 or
+    fp32, contiguous, on one GPU.  Returns (O, LSE): O in q's layout with
+    dtype ``out_dtype`` (default float32), LSE float32 [B,H,Nq].  The kernel
+    is enqueued on the current stream.
+    """
+    import torch
+
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {list(LAYOUTS)}")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must share dtype bfloat16 or float32")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    if layout == "BHND":
+        B, H, Nq, d = q.shape
+        Bk, Hk, Nk, dk = k.shape
+    else:
+        B, Nq, H, d = q.shape
+        Bk, Nk, Hk, dk = k.shape
+    if (Bk, Hk, dk) != (B, H, d):
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree for layout {layout}")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    elif out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor of q's shape, out_dtype and device")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != (B, H, Nq) or lse.dtype != torch.float32
+                              or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B,H,Nq] tensor on q's device")
+    in_dt = FA_BF16 if q.dtype == torch.bfloat16 else FA_F32
+    o_dt = FA_BF16 if out_dtype == torch.bfloat16 else FA_F32
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                    lse.data_ptr() if lse is not None else None, B, H, Nq, Nk, d,
+                    -1.0 if scale is None else float(scale), int(bool(causal)), LAYOUTS[layout],
+                    in_dt, o_dt, stream)
+    if st == FA_ERR_INVALID_ARG:
+        raise FaInvalidArgument(st, "invalid argument")
+    if st == FA_ERR_UNSUPPORTED:
+        raise FaUnsupported(st, "unsupported configuration")
+    if st != FA_OK:
+        raise FaError(st, "HIP launch failed")
+    return out, lse

@@ -1,0 +1,622 @@
+// fa_fwd.hip -- attention forward pass for gfx950 (AMD Instinct MI355X).
+//
+// Computes O = softmax(scale * Q K^T [causal]) V and the per-row log-sum-exp,
+// tile by tile with the online softmax, so the N x N score matrix never
+// leaves the compute unit.  Method sources (pages cited by site:
+// [nanhubrain] = nanhubrain.csdn.net, FlashAttention in CANN ops-transformer;
+// [ascendai] = ascendai.csdn.net, efficient attention in CANN ops-nn;
+// [pwwt] = www.pwwt.cn/news/2518640):
+//   * [nanhubrain] "tiling skeleton": query tiles outer, key/value tiles inner;
+//     scores of one tile pair exist only on chip; after the inner loop the
+//     accumulator is normalised by the row sum once and written once.
+//   * [nanhubrain] "online softmax mathematics" and [ascendai] 2.2: running row
+//     max m and row sum l; when m grows, the previous sum and accumulator are
+//     rescaled by exp(m_old - m_new), which is exact.
+//   * [ascendai] 3.2 (kernel): causal key blocks that lie entirely after the
+//     query block are skipped; [ascendai] 6.1: inside a block straddling the
+//     diagonal, key j is visible to query i iff j <= i.
+//   * [ascendai] 6.2/7.2 and [pwwt] "key differences" (third difference):
+//     accumulate in fp32.
+//
+// gfx950 design (the pages' Cube/Vector/UB design targets another machine;
+// only the method carries over):
+//   * one workgroup = NW wavefronts x 32 queries; grid over (batch*head,
+//     query tile), remapped so the tiles of one head run on one XCD (L2);
+//   * Q fragment held in VGPRs for the whole loop;
+//   * K and V tiles of 64 keys staged HBM -> VGPR -> LDS with 16-byte loads,
+//     double buffered (tile j+1 is in flight while tile j is computed), LDS
+//     rows XOR-swizzled in 16-byte units against bank conflicts;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (fp32 accumulate): a lane owns
+//     one query column, so the row max / row sum are in-lane plus one exchange
+//     between the two 32-lane halves;
+//   * P stays in registers: rounded to bf16 (RNE, v_cvt_pk_bf16_f32) and fed as
+//     the B operand of O^T = V^T P^T; V^T fragments come straight from the
+//     row-major LDS tile through ds_read_b64_tr_b16 (transposing LDS read);
+//   * exp2 with scale*log2(e) folded into one FMA; the running max follows
+//     every increase, so the row's dominant key always gets p = 1 exactly and
+//     its bf16 rounding is exact;
+//   * two row sums: l over the fp32 probabilities (for the log-sum-exp) and
+//     lt over the bf16-rounded probabilities that the P V product actually
+//     used (v_dot2c_f32_bf16 against (1,1)); O = acc / lt is then an exact
+//     convex combination of V rows, which removes the bias of the rounding
+//     when one key dominates;
+//   * epilogue: O = acc / lt in fp32 (or bf16), LSE = (m2 + log2 l) * ln 2.
+// A plain fp32 kernel (v_mfma_f32_32x32x2f32, P kept in fp32) serves fp32
+// inputs; there the running max moves only when a tile's max exceeds it by
+// more than 2^8 (exact: numerator and denominator share the stale max), which
+// makes rescaling the accumulator rare.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "fa355.h"
+
+namespace fa355 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// fp32 kernel: the running max moves only when a tile max exceeds it by more
+// than this (log2 units); probabilities then stay below 2^8 before the final
+// normalisation, which fp32 holds without loss.
+constexpr float kLazyRescale = 8.0f;
+
+struct FwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    long long q_sb, q_sh, q_sn;   // element strides of Q and O (batch, head, row)
+    long long k_sb, k_sh, k_sn;   // element strides of K and V
+    int H, Nq, Nk;
+    int n_qtiles;                 // ceil(Nq / rows per workgroup)
+    int BH;                       // B * H
+    float scale_log2;             // scale * log2(e)
+};
+
+// Workgroup id -> (batch*head, query tile).  Workgroups are dispatched round
+// robin over the 8 XCDs; when B*H is a multiple of 8, each XCD gets a
+// contiguous block of whole heads so one head's K/V stays in one XCD's L2.
+// Causal: heaviest (last) query tiles first.  A bijection in all cases.
+__device__ __forceinline__ void tile_of_block(int bid, int n_qtiles, int BH, bool causal,
+                                              int& bh, int& qt) {
+    if ((BH & 7) == 0) {
+        const int hpx = BH >> 3;
+        const int xcd = bid & 7;
+        const int s = bid >> 3;
+        if (causal) {
+            qt = n_qtiles - 1 - s / hpx;
+            bh = xcd * hpx + s % hpx;
+        } else {
+            bh = xcd * hpx + s / n_qtiles;
+            qt = s % n_qtiles;
+        }
+    } else if (causal) {
+        qt = n_qtiles - 1 - bid / BH;
+        bh = bid % BH;
+    } else {
+        bh = bid / n_qtiles;
+        qt = bid % n_qtiles;
+    }
+}
+
+// 16-byte-chunk swizzles of the LDS tiles (row = key within the tile, ch =
+// logical chunk of 8 bf16 along d).  K is read with ds_read_b128 by 32 lanes
+// on 32 consecutive rows at one chunk; V is read with ds_read_b64_tr_b16 on
+// 8 consecutive rows at 4 consecutive chunks.
+template <int D>
+__device__ __forceinline__ int k_swz(int row, int ch) {
+    if constexpr (D == 128) return ch ^ (row & 15);
+    else return ch ^ ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int row, int ch) {
+    if constexpr (D == 128) return ch ^ ((row & 3) << 2);
+    else return ch ^ (((row >> 1) & 1) << 2);
+}
+
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+    bf16x2 r = {(__bf16)a, (__bf16)b};   // v_cvt_pk_bf16_f32, round to nearest even
+    return __builtin_bit_cast(unsigned, r);
+}
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// acc + a.lo + a.hi for a packed pair of bf16 (exact products by 1.0, fp32 sum)
+__device__ __forceinline__ float add_bf16x2(unsigned a, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), one, acc, false);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 kernel
+//
+// D: head dim (64 or 128).  NW: waves per workgroup (32 queries each).
+// OUT_BF16: write O as bf16 instead of fp32.
+template <int D, int NW, bool CAUSAL, bool OUT_BF16>
+__global__ __launch_bounds__(NW * 64) void fa_fwd_bf16_kernel(FwdParams p) {
+    constexpr int BC = 64;              // keys per tile
+    constexpr int KB = BC / 32;         // 32-key sub-blocks per tile
+    constexpr int NT = NW * 64;         // threads
+    constexpr int BR = NW * 32;         // queries per workgroup
+    constexpr int DCH = D / 8;          // 16-byte chunks per row
+    constexpr int TILE_CH = BC * DCH;   // chunks per K (or V) tile
+    constexpr int CPT = TILE_CH / NT;   // chunks per thread per operand
+    constexpr int KK = D / 16;          // MFMA k-steps over d for S
+    constexpr int DB = D / 32;          // 32-wide d blocks of O
+    static_assert(TILE_CH % NT == 0, "tile must split evenly over threads");
+
+    // [stage][K|V][BC*DCH] 16-byte chunks
+    __shared__ u32x4 smem[2 * 2 * TILE_CH];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;
+    const int hi = lane >> 5;
+
+    int bh, qt;
+    tile_of_block(blockIdx.x, p.n_qtiles, p.BH, CAUSAL, bh, qt);
+    const int b = bh / p.H;
+    const int h = bh - b * p.H;
+
+    const int q_wg0 = qt * BR;
+    const int q_w0 = q_wg0 + wave * 32;       // first query of this wave
+    const int q = q_w0 + col;                 // this lane's query
+    const int Nq = p.Nq, Nk = p.Nk;
+
+    const __bf16* qbase = (const __bf16*)p.q + (long long)b * p.q_sb + (long long)h * p.q_sh;
+    const __bf16* kbase = (const __bf16*)p.k + (long long)b * p.k_sb + (long long)h * p.k_sh;
+    const __bf16* vbase = (const __bf16*)p.v + (long long)b * p.k_sb + (long long)h * p.k_sh;
+
+    // key range of this workgroup
+    int kv_end = Nk;
+    if (CAUSAL) {
+        const int q_last = min(q_wg0 + BR, Nq) - 1;
+        kv_end = min(Nk, q_last + 1);
+    }
+    const int n_kt = (kv_end + BC - 1) / BC;
+
+    // ---- Q fragment (B operand of S^T = K Q^T): lane holds Q[q][16kk + 8hi .. +7]
+    bf16x8 qreg[KK];
+    {
+        const bool ok = q < Nq;
+        const __bf16* qrow = qbase + (long long)(ok ? q : 0) * p.q_sn + hi * 8;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            u32x4 x = ok ? *(const u32x4*)(qrow + kk * 16) : (u32x4){0u, 0u, 0u, 0u};
+            qreg[kk] = __builtin_bit_cast(bf16x8, x);
+        }
+    }
+
+    // ---- staging registers and their (row, chunk) assignment
+    u32x4 kst[CPT], vst[CPT];
+    auto load_tile = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int idx = tid + i * NT;
+            const int row = idx / DCH;
+            const int ch = idx - row * DCH;
+            const int key = kt * BC + row;
+            if (key < Nk) {
+                const long long off = (long long)key * p.k_sn + ch * 8;
+                kst[i] = *(const u32x4*)(kbase + off);
+                vst[i] = *(const u32x4*)(vbase + off);
+            } else {
+                kst[i] = (u32x4){0u, 0u, 0u, 0u};
+                vst[i] = (u32x4){0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto store_tile = [&](int st) {
+        u32x4* ks = smem + (st * 2 + 0) * TILE_CH;
+        u32x4* vs = smem + (st * 2 + 1) * TILE_CH;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int idx = tid + i * NT;
+            const int row = idx / DCH;
+            const int ch = idx - row * DCH;
+            ks[row * DCH + k_swz<D>(row, ch)] = kst[i];
+            vs[row * DCH + v_swz<D>(row, ch)] = vst[i];
+        }
+    };
+
+    // ---- running state (per lane = per query; both halves hold the same m)
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    float m_run = -INFINITY;   // log2 domain
+    float l_run = 0.f;         // partial row sum of fp32 P over this lane's keys
+    float lt_run = 0.f;        // partial row sum of the bf16-rounded P
+    const float sl2 = p.scale_log2;
+
+    // V^T fragment addressing for ds_read_b64_tr_b16: within each 16-lane
+    // group, lane 4r+c fetches 4 consecutive d values of key row r; lane i
+    // then receives column i (one d value) of the 4 rows.
+    const int tg = lane >> 4;            // 16-lane group
+    const int ti = lane & 15;
+    const int tr_row = hi * 4 + (ti >> 2);             // key offset inside an 8-key group
+    const int tr_dd = 16 * (tg & 1) + 4 * (ti & 3);    // d offset inside a 32-wide d block
+
+    load_tile(0);
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const int st = kt & 1;
+        store_tile(st);
+        __syncthreads();
+        if (kt + 1 < n_kt) load_tile(kt + 1);
+
+        const int key0 = kt * BC;
+        // nothing to do for a wave whose rows are all padding, or (causal)
+        // whose queries all precede the tile
+        if (q_w0 >= Nq || (CAUSAL && key0 > q_w0 + 31)) continue;
+
+        const u32x4* ks = smem + (st * 2 + 0) * TILE_CH;
+        const lds_char* vs = (const lds_char*)(smem + (st * 2 + 1) * TILE_CH);
+
+        // ---- S^T = K Q^T for the tile: sacc[kb][r] = S[q][key0 + kb*32 + (r/4)*8 + hi*4 + r%4]
+        f32x16 sacc[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+            const int row = kb * 32 + col;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const u32x4 kx = ks[row * DCH + k_swz<D>(row, 2 * kk + hi)];
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, kx), qreg[kk], sacc[kb], 0, 0, 0);
+            }
+        }
+
+        // ---- mask (ragged tail, causal diagonal), row max
+        const bool need_mask = (key0 + BC > Nk) || (CAUSAL && key0 + BC - 1 > q_w0);
+        float mx = -INFINITY;
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = key0 + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+                    const bool ok = key < Nk && (!CAUSAL || key <= q);
+                    sacc[kb][r] = ok ? sacc[kb][r] : -INFINITY;
+                    mx = fmaxf(mx, sacc[kb][r]);
+                }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+        }
+        mx = fmaxf(mx, xor32(mx));
+        const float mt2 = (mx == -INFINITY) ? -INFINITY : mx * sl2;
+
+        // ---- max update and rescale (skipped by the whole wave when no row moved)
+        const bool move = mt2 > m_run;
+        const float m_new = move ? mt2 : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 1 when not moved, 0 first time
+        if (__builtin_amdgcn_ballot_w64(move)) {
+            l_run *= alpha;
+            lt_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+        m_run = m_new;
+
+        // ---- P = exp2(S*scale*log2e - m), row sums, pack to bf16
+        const float nm = -m_new;
+        unsigned pk[KB][8];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            float pv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], sl2, nm));
+                if (need_mask) e = (sacc[kb][r] == -INFINITY) ? 0.f : e;
+                pv[r] = e;
+                l_run += e;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                pk[kb][j] = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
+                lt_run = add_bf16x2(pk[kb][j], lt_run);
+            }
+        }
+
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const bf16x8 pb = __builtin_bit_cast(
+                    bf16x8, (u32x4){pk[kb][4 * u + 0], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]});
+                const int r0 = kb * 32 + 16 * u + tr_row;       // keys for slots 0..3
+                const int r1 = r0 + 8;                          // keys for slots 4..7
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const int dd = db * 32 + tr_dd;
+                    const int c = dd >> 3, w = (dd & 7) * 2;
+                    const lds_i16x4* a0 = (const lds_i16x4*)(vs + r0 * (D * 2) + v_swz<D>(r0, c) * 16 + w);
+                    const lds_i16x4* a1 = (const lds_i16x4*)(vs + r1 * (D * 2) + v_swz<D>(r1, c) * 16 + w);
+                    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
+                    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a1);
+                    const bf16x8 va = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[db], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // ---- epilogue
+    const float l_tot = l_run + xor32(l_run);
+    const float lt_tot = lt_run + xor32(lt_run);
+    if (q < Nq) {
+        const float inv = 1.0f / lt_tot;
+        char* obase = (char*)p.o;
+        const long long orow = (long long)b * p.q_sb + (long long)h * p.q_sh + (long long)q * p.q_sn;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int dd = db * 32 + g * 8 + hi * 4;
+                const float o0 = oacc[db][4 * g + 0] * inv, o1 = oacc[db][4 * g + 1] * inv;
+                const float o2 = oacc[db][4 * g + 2] * inv, o3 = oacc[db][4 * g + 3] * inv;
+                if constexpr (OUT_BF16) {
+                    u32x2 w = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+                    *(u32x2*)(obase + (orow + dd) * 2) = w;
+                } else {
+                    *(float4*)(obase + (orow + dd) * 4) = make_float4(o0, o1, o2, o3);
+                }
+            }
+        if (p.lse && hi == 0)
+            p.lse[(long long)bh * Nq + q] = (m_run + __log2f(l_tot)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: same method, v_mfma_f32_32x32x2f32, P kept in fp32, one
+// 32-key tile per iteration, single-buffered padded LDS.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fa_fwd_f32_kernel(FwdParams p) {
+    constexpr int NW = 4, BR = NW * 32, BC = 32, NT = NW * 64;
+    constexpr int LD = D + 1;            // padded LDS row (floats)
+    constexpr int DB = D / 32;
+    constexpr int C4 = D / 4;            // float4 chunks per row
+
+    __shared__ float ks[BC * LD];
+    __shared__ float vs[BC * LD];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;
+    const int hi = lane >> 5;
+
+    int bh, qt;
+    tile_of_block(blockIdx.x, p.n_qtiles, p.BH, CAUSAL, bh, qt);
+    const int b = bh / p.H;
+    const int h = bh - b * p.H;
+    const int q_wg0 = qt * BR;
+    const int q_w0 = q_wg0 + wave * 32;
+    const int q = q_w0 + col;
+    const int Nq = p.Nq, Nk = p.Nk;
+
+    const float* qbase = (const float*)p.q + (long long)b * p.q_sb + (long long)h * p.q_sh;
+    const float* kbase = (const float*)p.k + (long long)b * p.k_sb + (long long)h * p.k_sh;
+    const float* vbase = (const float*)p.v + (long long)b * p.k_sb + (long long)h * p.k_sh;
+
+    int kv_end = Nk;
+    if (CAUSAL) kv_end = min(Nk, min(q_wg0 + BR, Nq));
+    const int n_kt = (kv_end + BC - 1) / BC;
+
+    // Q fragment: lane holds Q[q][2kk + hi]
+    float qreg[D / 2];
+    {
+        const bool ok = q < Nq;
+        const float* qrow = qbase + (long long)(ok ? q : 0) * p.q_sn;
+#pragma unroll
+        for (int kk = 0; kk < D / 2; ++kk) qreg[kk] = ok ? qrow[2 * kk + hi] : 0.f;
+    }
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    const float sl2 = p.scale_log2;
+
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const int key0 = kt * BC;
+        __syncthreads();   // previous tile fully consumed
+        for (int idx = tid; idx < BC * C4; idx += NT) {
+            const int row = idx / C4, c4 = idx - row * C4;
+            const int key = key0 + row;
+            float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
+            if (key < Nk) {
+                const long long off = (long long)key * p.k_sn + c4 * 4;
+                kx = *(const float4*)(kbase + off);
+                vx = *(const float4*)(vbase + off);
+            }
+            float* kd = ks + row * LD + c4 * 4;
+            float* vd = vs + row * LD + c4 * 4;
+            kd[0] = kx.x; kd[1] = kx.y; kd[2] = kx.z; kd[3] = kx.w;
+            vd[0] = vx.x; vd[1] = vx.y; vd[2] = vx.z; vd[3] = vx.w;
+        }
+        __syncthreads();
+        if (q_w0 >= Nq || (CAUSAL && key0 > q_w0 + 31)) continue;
+
+        f32x16 sacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 2; ++kk)
+            sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[col * LD + 2 * kk + hi], qreg[kk], sacc, 0, 0, 0);
+
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = key0 + (r >> 2) * 8 + hi * 4 + (r & 3);
+            const bool ok = key < Nk && (!CAUSAL || key <= q);
+            sacc[r] = ok ? sacc[r] : -INFINITY;
+            mx = fmaxf(mx, sacc[r]);
+        }
+        mx = fmaxf(mx, xor32(mx));
+        const float mt2 = (mx == -INFINITY) ? -INFINITY : mx * sl2;
+        const bool move = mt2 > m_run + kLazyRescale;
+        const float m_new = move ? mt2 : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        if (__builtin_amdgcn_ballot_w64(move)) {
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+        m_run = m_new;
+
+        float pv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], sl2, -m_new));
+            pv[r] = (sacc[r] == -INFINITY) ? 0.f : e;
+            l_run += pv[r];
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = (r >> 2) * 8 + hi * 4 + (r & 3);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * LD + db * 32 + col], pv[r],
+                                                                 oacc[db], 0, 0, 0);
+            }
+    }
+
+    const float l_tot = l_run + xor32(l_run);
+    if (q < Nq) {
+        const float inv = 1.0f / l_tot;
+        float* obase = (float*)p.o + (long long)b * p.q_sb + (long long)h * p.q_sh + (long long)q * p.q_sn;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int dd = db * 32 + g * 8 + hi * 4;
+                *(float4*)(obase + dd) = make_float4(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
+                                                     oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+            }
+        if (p.lse && hi == 0)
+            p.lse[(long long)bh * Nq + q] = (m_run + __log2f(l_tot)) * kLn2;
+    }
+}
+
+}  // namespace fa355
+
+// ---------------------------------------------------------------------------
+// C ABI
+
+using namespace fa355;
+
+namespace {
+
+constexpr int kWavesBf16 = 4;   // queries per workgroup = 32 * waves
+constexpr int kWavesF32 = 4;
+
+template <int D, bool CAUSAL, bool OUT_BF16>
+hipError_t launch_bf16(const FwdParams& p, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, kWavesBf16, CAUSAL, OUT_BF16>), dim3(grid),
+                       dim3(kWavesBf16 * 64), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_f32(const FwdParams& p, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), dim3(grid), dim3(kWavesF32 * 64), 0, s, p);
+    return hipGetLastError();
+}
+
+bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" int fa_abi_version(void) { return FA355_ABI_VERSION; }
+
+extern "C" const char* fa_status_str(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+        case FA_ERR_HIP: return "FA_ERR_HIP";
+        default: return "FA_UNKNOWN_STATUS";
+    }
+}
+
+extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                            int layout, int in_dtype, int o_dtype, void* stream) {
+    // ---- validation: no HIP call before it passes
+    if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (layout != FA_BHND && layout != FA_BSND) return FA_ERR_INVALID_ARG;
+    if (in_dtype != FA_BF16 && in_dtype != FA_F32) return FA_ERR_INVALID_ARG;
+    if (o_dtype != FA_BF16 && o_dtype != FA_F32) return FA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FA_ERR_INVALID_ARG;
+    if (lse && !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+    if (scale != scale || fabsf(scale) == INFINITY) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (in_dtype == FA_F32 && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+
+    const int rows_per_wg = 32 * (in_dtype == FA_BF16 ? kWavesBf16 : kWavesF32);
+    const long long n_qtiles = ((long long)Nq + rows_per_wg - 1) / rows_per_wg;
+    const long long grid = n_qtiles * B * H;
+    if ((long long)B * H > INT32_MAX || grid > INT32_MAX) return FA_ERR_UNSUPPORTED;
+
+    if (scale < 0.f) scale = 1.0f / sqrtf((float)d);
+
+    FwdParams p;
+    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+    const long long D = d;
+    if (layout == FA_BHND) {
+        p.q_sb = (long long)H * Nq * D; p.q_sh = (long long)Nq * D; p.q_sn = D;
+        p.k_sb = (long long)H * Nk * D; p.k_sh = (long long)Nk * D; p.k_sn = D;
+    } else {
+        p.q_sb = (long long)Nq * H * D; p.q_sh = D; p.q_sn = (long long)H * D;
+        p.k_sb = (long long)Nk * H * D; p.k_sh = D; p.k_sn = (long long)H * D;
+    }
+    p.H = H; p.Nq = Nq; p.Nk = Nk;
+    p.n_qtiles = (int)n_qtiles;
+    p.BH = B * H;
+    p.scale_log2 = scale * kLog2e;
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool c = causal != 0;
+    hipError_t err;
+    if (in_dtype == FA_BF16) {
+        const bool ob = o_dtype == FA_BF16;
+        if (d == 128) {
+            err = c ? (ob ? launch_bf16<128, true, true>(p, (int)grid, s) : launch_bf16<128, true, false>(p, (int)grid, s))
+                    : (ob ? launch_bf16<128, false, true>(p, (int)grid, s) : launch_bf16<128, false, false>(p, (int)grid, s));
+        } else {
+            err = c ? (ob ? launch_bf16<64, true, true>(p, (int)grid, s) : launch_bf16<64, true, false>(p, (int)grid, s))
+                    : (ob ? launch_bf16<64, false, true>(p, (int)grid, s) : launch_bf16<64, false, false>(p, (int)grid, s));
+        }
+    } else {
+        if (d == 128) err = c ? launch_f32<128, true>(p, (int)grid, s) : launch_f32<128, false>(p, (int)grid, s);
+        else err = c ? launch_f32<64, true>(p, (int)grid, s) : launch_f32<64, false>(p, (int)grid, s);
+    }
+    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}

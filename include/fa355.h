@@ -27,6 +27,13 @@
 extern "C" {
 #endif
 
+/* Symbols of the shared library (built with hidden default visibility). */
+#if defined(__GNUC__) || defined(__clang__)
+#define FA355_API __attribute__((visibility("default")))
+#else
+#define FA355_API
+#endif
+
 typedef enum fa_status {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad enum, misalignment, NaN/inf scale */
@@ -78,15 +85,15 @@ typedef enum fa_dtype {
  * end.  Validation failures return before any HIP call.  Results are
  * deterministic: a fixed reduction order, no atomics.
  */
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                 int B, int H, int Nq, int Nk, int d, float scale, int causal,
-                 int layout, int in_dtype, int o_dtype, void* stream);
+FA355_API fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                           int layout, int in_dtype, int o_dtype, void* stream);
 
 /* A static, human-readable name for a status code (never NULL). */
-const char* fa_status_str(int status);
+FA355_API const char* fa_status_str(int status);
 
 /* ABI version of this header (incremented on incompatible change). */
-int fa_abi_version(void);
+FA355_API int fa_abi_version(void);
 
 #define FA355_ABI_VERSION 1
 

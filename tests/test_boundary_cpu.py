@@ -1,0 +1,120 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and every argument-validation path returns its status before any HIP
+call (so no compute is attempted here)."""
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_attention_112_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa355.h")
+
+
+def header_text():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def declared_functions():
+    return set(re.findall(r"FA355_API\s+[\w\s\*]+?\b(\w+)\s*\(", header_text()))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load()
+    names = declared_functions()
+    assert names == set(fa.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert names <= exported
+    for n in names:
+        assert hasattr(lib, n)
+    # nothing else leaks out of the library as a function symbol
+    assert exported == names
+
+
+def test_header_constants_match_binding():
+    t = header_text()
+    consts = {k: int(v) for k, v in re.findall(r"\b(FA_[A-Z0-9_]+)\s*=\s*(\d+)", t)}
+    for name, val in consts.items():
+        assert getattr(fa, name) == val, name
+    assert int(re.search(r"#define FA355_ABI_VERSION (\d+)", t).group(1)) == fa.ABI_VERSION
+    assert fa.load().fa_abi_version() == fa.ABI_VERSION
+
+
+def test_status_strings():
+    assert fa.fa_status_str(0) == "FA_OK"
+    assert fa.fa_status_str(1) == "FA_ERR_INVALID_ARG"
+    assert fa.fa_status_str(2) == "FA_ERR_UNSUPPORTED"
+    assert fa.fa_status_str(3) == "FA_ERR_HIP"
+    assert fa.fa_status_str(99) == "FA_UNKNOWN_STATUS"
+
+
+# Fake, 16-byte-aligned, never-dereferenced addresses: validation rejects every
+# case below before anything would touch them.
+P = 0x10000
+GOOD = dict(q=P, k=P + 0x1000, v=P + 0x2000, o=P + 0x3000, lse=P + 0x4000, B=1, H=2, Nq=16,
+            Nk=16, d=64, scale=-1.0, causal=0, layout=fa.FA_BHND, in_dtype=fa.FA_BF16,
+            o_dtype=fa.FA_F32, stream=None)
+
+
+def call(**changes):
+    a = dict(GOOD, **changes)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"],
+                     a["d"], a["scale"], a["causal"], a["layout"], a["in_dtype"], a["o_dtype"],
+                     a["stream"])
+
+
+@pytest.mark.parametrize("changes,status", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(k=0), fa.FA_ERR_INVALID_ARG),
+    (dict(v=0), fa.FA_ERR_INVALID_ARG),
+    (dict(o=0), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=0), fa.FA_ERR_INVALID_ARG),
+    (dict(layout=2), fa.FA_ERR_INVALID_ARG),
+    (dict(in_dtype=7), fa.FA_ERR_INVALID_ARG),
+    (dict(o_dtype=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(q=P + 8), fa.FA_ERR_INVALID_ARG),          # misaligned
+    (dict(o=P + 0x3004), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=P + 0x4002), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=math.nan), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=math.inf), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(in_dtype=fa.FA_F32, o_dtype=fa.FA_BF16), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=1 << 16, H=1 << 16), fa.FA_ERR_UNSUPPORTED),   # grid beyond 2^31 workgroups
+])
+def test_validation_returns_before_launch(changes, status):
+    assert call(**changes) == status
+
+
+def test_python_wrapper_validates_without_gpu():
+    import torch
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        fa.fwd(x, x, x)                        # CPU tensors are refused
+    with pytest.raises(ValueError):
+        fa.fwd(x, x, x, layout="NHWC")
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        fa.load.__wrapped__(str(tmp_path / "nope.so")) if hasattr(fa.load, "__wrapped__") else \
+            _load_fresh(str(tmp_path / "nope.so"))
+
+
+def _load_fresh(path):
+    saved = fa._lib
+    fa._lib = None
+    try:
+        fa.load(path)
+    finally:
+        fa._lib = saved

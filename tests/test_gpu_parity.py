@@ -1,0 +1,255 @@
+"""GPU parity: the HIP path (through the C ABI binding) against the fp64 oracle
+on the same seeded inputs.
+
+* reduced sizes of every workload, compared element by element (several tiles
+  and a ragged tail in both sequence dimensions);
+* the full-size workloads in the launch configuration the benchmark times,
+  compared on sampled rows the oracle computes one by one, plus properties
+  that hold on every row at any size (finite; O inside the per-column range of
+  the visible V rows; LSE between the diagonal / first-key score and an upper
+  bound from the norms);
+* edge shapes, closed forms, layouts, output dtype, determinism, streams.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_attention_112_amd import inputs as I
+from gpu_common import (BF16_TOL, F32_TOL, check, errors, log, require_gpu, run_gpu, to_bhnd,
+                        tol_for, upload)
+
+pytestmark = pytest.mark.gpu
+
+W = I.WORKLOADS
+
+
+def _full_compare(w, out_dtype=None, seed_base=None):
+    import torch
+    require_gpu()
+    log(f"case {w.name} B{w.B} H{w.H} Nq{w.Nq} Nk{w.Nk} d{w.d} {w.dtype} {w.layout} causal={w.causal}")
+    inp = I.make_inputs(w, seed_base=seed_base)
+    tq, tk, tv = upload(inp)
+    o, lse = run_gpu(w, tq, tk, tv, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_fwd(inp.q, inp.k, inp.v, scale=w.scale, causal=w.causal,
+                                     layout=w.layout)
+    err = errors(to_bhnd(o, w.layout), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref)
+    check(err, tol_for(w, out_dtype), w.name)
+    return err
+
+
+# ---------------------------------------------------------------------------
+# reduced sizes, element by element
+
+REDUCED = {
+    "tiny_f32": W["tiny_f32"],
+    "llama_prefill_causal": W["llama_prefill_causal"].scaled(H=4, Nq=1000, Nk=1000),
+    "selfattn_b4h32n8k": W["selfattn_b4h32n8k"].scaled(B=2, H=2, Nq=777, Nk=777),
+    "sd_crossattn": W["sd_crossattn"],                     # full size: oracle takes ~seconds
+    "long_causal_128k": W["long_causal_128k"].scaled(H=2, Nq=3000, Nk=3000),
+}
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_workload_reduced_full_compare(name):
+    _full_compare(REDUCED[name])
+
+
+def test_bf16_output_option():
+    import torch
+    _full_compare(REDUCED["selfattn_b4h32n8k"], out_dtype=torch.bfloat16)
+    _full_compare(REDUCED["llama_prefill_causal"], out_dtype=torch.bfloat16)
+
+
+# ---------------------------------------------------------------------------
+# full sizes: sampled rows + properties on every row
+
+def _properties_all_rows(w, tq, tk, tv, o, lse):
+    """Finite; each O element within [min, max] of its column over the visible
+    V rows (widened by the bf16 rounding of P); LSE >= scale*q_i.k_0 and
+    (causal) >= scale*q_i.k_i; LSE <= scale*|q_i|*max_j|k_j| + ln(n_visible)."""
+    import torch
+    bhnd = (lambda t: t) if w.layout == "BHND" else (lambda t: t.transpose(1, 2))
+    Of = bhnd(o).float()
+    assert torch.isfinite(Of).all() and torch.isfinite(lse).all()
+    V = bhnd(tv).float()
+    K = bhnd(tk).float()
+    Q = bhnd(tq).float()
+    if w.causal:
+        vmax = torch.cummax(V, dim=2).values
+        vmin = torch.cummin(V, dim=2).values
+        n = min(w.Nq, w.Nk)
+        vmax, vmin = vmax[:, :, :n], vmin[:, :, :n]
+        if w.Nq > n:   # rows past Nk see every key
+            vmax = torch.cat([vmax, vmax[:, :, -1:].expand(-1, -1, w.Nq - n, -1)], 2)
+            vmin = torch.cat([vmin, vmin[:, :, -1:].expand(-1, -1, w.Nq - n, -1)], 2)
+    else:
+        vmax = V.amax(dim=2, keepdim=True)
+        vmin = V.amin(dim=2, keepdim=True)
+    slack = 2.0 ** -8 * V.abs().amax().item() + 1e-3
+    assert (Of <= vmax + slack).all(), "O above the range of visible V rows"
+    assert (Of >= vmin - slack).all(), "O below the range of visible V rows"
+    del vmax, vmin, Of
+    s0 = w.scale * (Q * K[:, :, :1]).sum(-1)
+    assert (lse >= s0 - 1e-3).all(), "LSE below the score of key 0"
+    if w.causal:
+        n = min(w.Nq, w.Nk)
+        sd = w.scale * (Q[:, :, :n] * K[:, :, :n]).sum(-1)
+        assert (lse[:, :, :n] >= sd - 1e-3).all(), "LSE below the diagonal score"
+        nvis = torch.clamp(torch.arange(1, w.Nq + 1, device=lse.device), max=w.Nk).float()
+    else:
+        nvis = torch.full((w.Nq,), float(w.Nk), device=lse.device)
+    kmax = K.norm(dim=-1).amax(dim=-1, keepdim=True)
+    ub = w.scale * Q.norm(dim=-1) * kmax + torch.log(nvis)
+    assert (lse <= ub + 1e-3).all(), "LSE above the norm bound"
+
+
+@pytest.mark.parametrize("name", ["llama_prefill_causal", "selfattn_b4h32n8k", "long_causal_128k"])
+def test_workload_full_size_sampled(name):
+    import torch
+    require_gpu()
+    w = W[name]
+    log(f"case {w.name} full size B{w.B} H{w.H} N{w.Nq} d{w.d} causal={w.causal}")
+    inp = I.make_inputs(w)
+    tq, tk, tv = upload(inp)
+    o, lse = run_gpu(w, tq, tk, tv)
+    torch.cuda.synchronize()
+    rows = I.sample_rows(w, 48, peaked=inp.peaked)
+    o_ref, lse_ref = oracle.attn_fwd(inp.q, inp.k, inp.v, scale=w.scale, causal=w.causal,
+                                     layout=w.layout, rows=rows)
+    rows_t = torch.from_numpy(rows.astype(np.int64)).cuda()
+    if w.layout == "BHND":
+        o_s = o.index_select(2, rows_t)
+    else:
+        o_s = o.index_select(1, rows_t).transpose(1, 2)
+    err = errors(o_s.double().cpu().numpy(), lse.index_select(2, rows_t).double().cpu().numpy(),
+                 o_ref, lse_ref)
+    check(err, BF16_TOL, f"{name} ({len(rows)} sampled rows x {w.B * w.H} heads)")
+    _properties_all_rows(w, tq, tk, tv, o, lse)
+
+
+# ---------------------------------------------------------------------------
+# edge shapes
+
+EDGE_N = [1, 15, 63, 64, 65, 127, 129]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_edge_shapes(d, causal, dtype):
+    import torch
+    require_gpu()
+    worst = {}
+    for i, nq in enumerate(EDGE_N):
+        for j, nk in enumerate(EDGE_N):
+            if (i + j) % 2 and not (nq == nk):    # half of the off-diagonal pairs
+                continue
+            layout = "BSND" if (i + j) % 3 == 0 else "BHND"
+            w = I.Workload(90, "edge", 1, 3, nq, nk, d, dtype, layout, causal)
+            inp = I.make_inputs(w, seed_base=90000 + 100 * i + j)
+            tq, tk, tv = upload(inp)
+            o, lse = run_gpu(w, tq, tk, tv)
+            torch.cuda.synchronize()
+            o_ref, lse_ref = oracle.attn_fwd(inp.q, inp.k, inp.v, scale=w.scale, causal=causal,
+                                             layout=layout)
+            err = errors(to_bhnd(o, layout), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref)
+            tol = F32_TOL if dtype == "f32" else BF16_TOL
+            check(err, tol, f"edge Nq={nq} Nk={nk} d={d} {dtype} {layout} causal={causal}")
+            worst[(nq, nk)] = err["o_max"]
+
+
+def test_large_head_count_and_batch():
+    """B*H not a multiple of 8 (the other block-to-tile mapping) and B > 1."""
+    _full_compare(I.Workload(91, "bh_odd", 3, 5, 300, 200, 128, "bf16", "BSND", True))
+    _full_compare(I.Workload(92, "bh_odd2", 3, 5, 300, 200, 64, "bf16", "BHND", False))
+
+
+# ---------------------------------------------------------------------------
+# closed forms on the GPU
+
+def test_closed_forms():
+    import torch
+    import exact_attention_112_amd as fa
+    require_gpu()
+    B, H, N, d = 1, 2, 200, 128
+    # all ones: O == 1, LSE = scale*d + ln|Vis|
+    ones = torch.ones(B, H, N, d, dtype=torch.bfloat16, device="cuda")
+    for causal in (False, True):
+        o, lse = fa.fwd(ones, ones, ones, causal=causal)
+        assert (o - 1).abs().max().item() < 1e-6
+        nvis = torch.arange(1, N + 1, device="cuda").float() if causal else torch.full((N,), float(N), device="cuda")
+        ref = math.sqrt(d) + torch.log(nvis)
+        assert (lse - ref).abs().max().item() < 1e-4
+    # scale 0: mean of the visible V rows
+    g = torch.Generator(device="cuda").manual_seed(5)
+    q = torch.randn(B, H, N, d, device="cuda", generator=g).bfloat16()
+    k = torch.randn(B, H, N, d, device="cuda", generator=g).bfloat16()
+    v = torch.randn(B, H, N, d, device="cuda", generator=g).bfloat16()
+    for causal in (False, True):
+        o, lse = fa.fwd(q, k, v, causal=causal, scale=0.0)
+        vf = v.double()
+        if causal:
+            ref = torch.cumsum(vf, 2) / torch.arange(1, N + 1, device="cuda").double()[:, None]
+        else:
+            ref = vf.mean(2, keepdim=True).expand_as(vf)
+        assert (o.double() - ref).abs().max().item() < 1e-2
+    # dominant key: with q >= 0 and key 37 = 32 in every coordinate, its score
+    # exceeds every other by > 100, so O is V row 37
+    qpos = q.abs()
+    k3 = k.clone()
+    k3[:, :, 37] = 32.0
+    o, lse = fa.fwd(qpos, k3, v)
+    assert (o - v[:, :, 37:38].float()).abs().max().item() < 1e-3
+
+
+# ---------------------------------------------------------------------------
+# API behaviour
+
+def test_lse_optional_and_deterministic():
+    import torch
+    import exact_attention_112_amd as fa
+    require_gpu()
+    w = REDUCED["long_causal_128k"]
+    inp = I.make_inputs(w)
+    tq, tk, tv = upload(inp)
+    o1, l1 = fa.fwd(tq, tk, tv, causal=True, layout=w.layout)
+    o2, l2 = fa.fwd(tq, tk, tv, causal=True, layout=w.layout)
+    o3, l3 = fa.fwd(tq, tk, tv, causal=True, layout=w.layout, return_lse=False)
+    torch.cuda.synchronize()
+    assert l3 is None
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1, o3)
+
+
+def test_runs_on_caller_stream():
+    import torch
+    import exact_attention_112_amd as fa
+    require_gpu()
+    w = REDUCED["selfattn_b4h32n8k"]
+    inp = I.make_inputs(w)
+    tq, tk, tv = upload(inp)
+    ref_o, ref_l = fa.fwd(tq, tk, tv)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = torch.full_like(ref_o, float("nan"))
+        o, l = fa.fwd(tq, tk, tv, out=out)
+        o2 = o * 1.0          # consumer on the same stream sees the result
+    s.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(o2, ref_o) and torch.equal(l, ref_l)
+
+
+def test_wrapper_rejects_bad_tensors():
+    import torch
+    import exact_attention_112_amd as fa
+    require_gpu()
+    x = torch.zeros(1, 2, 16, 96, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(NotImplementedError):
+        fa.fwd(x, x, x)          # d = 96
+    y = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        fa.fwd(y, y.float(), y)  # mixed dtypes
+    with pytest.raises(ValueError):
+        fa.fwd(y.transpose(2, 3), y, y)
