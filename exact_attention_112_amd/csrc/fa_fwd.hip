@@ -144,25 +144,145 @@ __device__ __forceinline__ float add_bf16x2(unsigned a, float acc) {
 //
 // D: head dim (64 or 128).  NW: waves per workgroup (32 queries each).
 // OUT_BF16: write O as bf16 instead of fp32.
-template <int D, int NW, bool CAUSAL, bool OUT_BF16>
-__global__ __launch_bounds__(NW * 64) void fa_fwd_bf16_kernel(FwdParams p) {
-    constexpr int BC = 64;              // keys per tile
-    constexpr int KB = BC / 32;         // 32-key sub-blocks per tile
-    constexpr int NT = NW * 64;         // threads
-    constexpr int BR = NW * 32;         // queries per workgroup
-    constexpr int DCH = D / 8;          // 16-byte chunks per row
-    constexpr int TILE_CH = BC * DCH;   // chunks per K (or V) tile
-    constexpr int CPT = TILE_CH / NT;   // chunks per thread per operand
-    constexpr int KK = D / 16;          // MFMA k-steps over d for S
-    constexpr int DB = D / 32;          // 32-wide d blocks of O
-    static_assert(TILE_CH % NT == 0, "tile must split evenly over threads");
 
-    // [stage][K|V][BC*DCH] 16-byte chunks
+// Per-wave state of the online softmax for its 32 queries (one per lane; the
+// two 32-lane halves hold the same query and split its keys).
+template <int D>
+struct RowState {
+    f32x16 oacc[D / 32];   // O^T accumulator: oacc[db][r] = O[q][db*32 + (r/4)*8 + hi*4 + r%4]
+    float m;               // running max of scale*log2(e)*s
+    float l;               // partial sum of fp32 P over this lane's keys
+    float lt;              // partial sum of bf16-rounded P
+};
+
+// One 64-key tile for one wave: S^T = K Q^T, (mask), online softmax, O^T += V^T P^T.
+//   ks:   K tile in LDS, [64][D/8] 16-byte chunks, swizzled by k_swz
+//   vs:   V tile in LDS, same shape, swizzled by v_swz (byte pointer)
+//   key0: first key of the tile; q: this lane's query (masking only)
+template <int D, bool MASK, bool CAUSAL>
+__device__ __forceinline__ void tile_step(RowState<D>& st, const bf16x8 (&qreg)[D / 16],
+                                          const u32x4* __restrict__ ks, const lds_char* vs,
+                                          int key0, int q, int Nk, float sl2,
+                                          int col, int hi, int tr_row, int tr_dd) {
+    constexpr int DCH = D / 8, KK = D / 16, DB = D / 32;
+
+    // ---- S^T for the two 32-key halves of the tile
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+        const int row = kb * 32 + col;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const u32x4 kx = ks[row * DCH + k_swz<D>(row, 2 * kk + hi)];
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qreg[kk],
+                                                               sacc[kb], 0, 0, 0);
+        }
+    }
+
+    // ---- mask, row max (in-lane, then across the two halves)
+    if constexpr (MASK) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = key0 + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+                const bool ok = key < Nk && (!CAUSAL || key <= q);
+                sacc[kb][r] = ok ? sacc[kb][r] : -INFINITY;
+            }
+    }
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = fmaxf(mx, xor32(mx));
+    // scale >= 0, so the max of the scaled scores is the scaled max
+    const float mt2 = (MASK && mx == -INFINITY) ? -INFINITY : mx * sl2;
+
+    // ---- move the max and rescale (skipped by the whole wave when no row moved)
+    const bool move = mt2 > st.m;
+    const float m_new = move ? mt2 : st.m;
+    if (__builtin_amdgcn_ballot_w64(move)) {
+        const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // 1 if not moved, 0 the first time
+        st.l *= alpha;
+        st.lt *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
+        st.m = m_new;
+    }
+
+    // ---- P = exp2(s*scale*log2e - m); sums; bf16 pack
+    const float nm = -st.m;
+    unsigned pk[2][8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][2 * j], sl2, nm));
+            float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][2 * j + 1], sl2, nm));
+            if constexpr (MASK) {   // -inf * 0 (scale 0) would be NaN: force masked keys to 0
+                e0 = sacc[kb][2 * j] == -INFINITY ? 0.f : e0;
+                e1 = sacc[kb][2 * j + 1] == -INFINITY ? 0.f : e1;
+            }
+            st.l += e0;
+            st.l += e1;
+            pk[kb][j] = pack_bf16x2(e0, e1);
+            st.lt = add_bf16x2(pk[kb][j], st.lt);
+        }
+    }
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const bf16x8 pb = __builtin_bit_cast(
+                bf16x8, (u32x4){pk[kb][4 * u + 0], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]});
+            const int r0 = kb * 32 + 16 * u + tr_row;    // keys of P slots 0..3
+            const int r1 = r0 + 8;                       // keys of P slots 4..7
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int dd = db * 32 + tr_dd;
+                const int c = dd >> 3, w = (dd & 7) * 2;
+                const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4*)(vs + r0 * (D * 2) + v_swz<D>(r0, c) * 16 + w));
+                const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4*)(vs + r1 * (D * 2) + v_swz<D>(r1, c) * 16 + w));
+                const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+                st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, st.oacc[db], 0, 0, 0);
+            }
+        }
+    }
+}
+
+template <int D, int NW>
+struct Bf16Cfg {
+    static constexpr int BC = 64;                 // keys per tile
+    static constexpr int NT = NW * 64;            // threads per workgroup
+    static constexpr int BR = NW * 32;            // queries per workgroup
+    static constexpr int DCH = D / 8;             // 16-byte chunks per row
+    static constexpr int TILE_CH = BC * DCH;      // chunks per K (or V) tile
+    static constexpr int LD_PER_WAVE = TILE_CH / 64 / NW;   // direct-to-LDS loads per wave per operand
+    static_assert(TILE_CH % (64 * NW) == 0, "tile must split evenly over the waves");
+};
+
+template <int D, int NW, bool CAUSAL, bool OUT_BF16>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_bf16_kernel(FwdParams p) {
+    using C = Bf16Cfg<D, NW>;
+    constexpr int BC = C::BC, BR = C::BR, DCH = C::DCH, TILE_CH = C::TILE_CH;
+    constexpr int KK = D / 16, DB = D / 32;
+
+    // [stage][K|V][TILE_CH] 16-byte chunks
     __shared__ u32x4 smem[2 * 2 * TILE_CH];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int col = lane & 31;
     const int hi = lane >> 5;
 
@@ -172,21 +292,26 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_bf16_kernel(FwdParams p) {
     const int h = bh - b * p.H;
 
     const int q_wg0 = qt * BR;
-    const int q_w0 = q_wg0 + wave * 32;       // first query of this wave
-    const int q = q_w0 + col;                 // this lane's query
+    const int q_w0 = q_wg0 + wave * 32;   // first query of this wave
+    const int q = q_w0 + col;             // this lane's query
     const int Nq = p.Nq, Nk = p.Nk;
 
     const __bf16* qbase = (const __bf16*)p.q + (long long)b * p.q_sb + (long long)h * p.q_sh;
     const __bf16* kbase = (const __bf16*)p.k + (long long)b * p.k_sb + (long long)h * p.k_sh;
     const __bf16* vbase = (const __bf16*)p.v + (long long)b * p.k_sb + (long long)h * p.k_sh;
 
-    // key range of this workgroup
+    // Keys this workgroup needs.  Tiles [0, n_full) need no mask for any wave
+    // (every key < Nk and, causal, <= the workgroup's first query); the rest
+    // go through the masked step, and a wave skips the tiles past its last
+    // query (causal) or all of them if its rows are all padding.
     int kv_end = Nk;
-    if (CAUSAL) {
-        const int q_last = min(q_wg0 + BR, Nq) - 1;
-        kv_end = min(Nk, q_last + 1);
-    }
+    if (CAUSAL) kv_end = min(Nk, min(q_wg0 + BR, Nq));
     const int n_kt = (kv_end + BC - 1) / BC;
+    int n_full = Nk / BC;
+    if (CAUSAL) n_full = min(n_full, (q_wg0 + 1) / BC);
+    n_full = min(n_full, n_kt);
+    int n_kt_wave = q_w0 < Nq ? n_kt : 0;
+    if (CAUSAL && q_w0 < Nq) n_kt_wave = min(n_kt, min(q_w0 + 31, Nq - 1) / BC + 1);
 
     // ---- Q fragment (B operand of S^T = K Q^T): lane holds Q[q][16kk + 8hi .. +7]
     bf16x8 qreg[KK];
@@ -200,171 +325,79 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_bf16_kernel(FwdParams p) {
         }
     }
 
-    // ---- staging registers and their (row, chunk) assignment
-    u32x4 kst[CPT], vst[CPT];
-    auto load_tile = [&](int kt) {
+    // ---- direct HBM -> LDS staging.  Each wave instruction writes 64
+    // consecutive 16-byte LDS chunks; lane i of load j fills physical chunk
+    // pc = (wave*LD_PER_WAVE + j)*64 + i, i.e. row pc/DCH, swizzled chunk pc%DCH,
+    // so it fetches the logical chunk (pc%DCH) ^ swz(row).  Keys past Nk are
+    // clamped to Nk-1: their scores are masked, and V rows stay finite.
+    int ld_row[C::LD_PER_WAVE], ld_kch[C::LD_PER_WAVE], ld_vch[C::LD_PER_WAVE];
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int idx = tid + i * NT;
-            const int row = idx / DCH;
-            const int ch = idx - row * DCH;
-            const int key = kt * BC + row;
-            if (key < Nk) {
-                const long long off = (long long)key * p.k_sn + ch * 8;
-                kst[i] = *(const u32x4*)(kbase + off);
-                vst[i] = *(const u32x4*)(vbase + off);
-            } else {
-                kst[i] = (u32x4){0u, 0u, 0u, 0u};
-                vst[i] = (u32x4){0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    auto store_tile = [&](int st) {
-        u32x4* ks = smem + (st * 2 + 0) * TILE_CH;
-        u32x4* vs = smem + (st * 2 + 1) * TILE_CH;
+    for (int j = 0; j < C::LD_PER_WAVE; ++j) {
+        const int pc = (wave * C::LD_PER_WAVE + j) * 64 + lane;
+        const int row = pc / DCH, ch = pc - (pc / DCH) * DCH;
+        ld_row[j] = row;
+        ld_kch[j] = k_swz<D>(row, ch);   // XOR swizzles are their own inverse
+        ld_vch[j] = v_swz<D>(row, ch);
+    }
+    lds_char* const lds = (lds_char*)smem;
+    auto issue_tile = [&](int kt, int stg) {
+        lds_char* kdst = lds + (stg * 2 + 0) * TILE_CH * 16 + wave * C::LD_PER_WAVE * 1024;
+        lds_char* vdst = lds + (stg * 2 + 1) * TILE_CH * 16 + wave * C::LD_PER_WAVE * 1024;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int idx = tid + i * NT;
-            const int row = idx / DCH;
-            const int ch = idx - row * DCH;
-            ks[row * DCH + k_swz<D>(row, ch)] = kst[i];
-            vs[row * DCH + v_swz<D>(row, ch)] = vst[i];
+        for (int j = 0; j < C::LD_PER_WAVE; ++j) {
+            const int key = min(kt * BC + ld_row[j], Nk - 1);
+            const long long roff = (long long)key * p.k_sn;
+            __builtin_amdgcn_global_load_lds((const void*)(kbase + roff + ld_kch[j] * 8),
+                                             (__attribute__((address_space(3))) void*)(kdst + j * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(vbase + roff + ld_vch[j] * 8),
+                                             (__attribute__((address_space(3))) void*)(vdst + j * 1024), 16, 0, 0);
         }
     };
 
-    // ---- running state (per lane = per query; both halves hold the same m)
-    f32x16 oacc[DB];
+    RowState<D> st;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-    float m_run = -INFINITY;   // log2 domain
-    float l_run = 0.f;         // partial row sum of fp32 P over this lane's keys
-    float lt_run = 0.f;        // partial row sum of the bf16-rounded P
+        for (int r = 0; r < 16; ++r) st.oacc[db][r] = 0.f;
+    st.m = -INFINITY;
+    st.l = 0.f;
+    st.lt = 0.f;
     const float sl2 = p.scale_log2;
 
     // V^T fragment addressing for ds_read_b64_tr_b16: within each 16-lane
     // group, lane 4r+c fetches 4 consecutive d values of key row r; lane i
     // then receives column i (one d value) of the 4 rows.
-    const int tg = lane >> 4;            // 16-lane group
-    const int ti = lane & 15;
-    const int tr_row = hi * 4 + (ti >> 2);             // key offset inside an 8-key group
-    const int tr_dd = 16 * (tg & 1) + 4 * (ti & 3);    // d offset inside a 32-wide d block
+    const int tg = lane >> 4, ti = lane & 15;
+    const int tr_row = hi * 4 + (ti >> 2);            // key offset inside an 8-key group
+    const int tr_dd = 16 * (tg & 1) + 4 * (ti & 3);   // d offset inside a 32-wide d block
 
-    load_tile(0);
-    for (int kt = 0; kt < n_kt; ++kt) {
-        const int st = kt & 1;
-        store_tile(st);
+    // Two loops with the same barrier structure, so the unmasked one has no
+    // branch around its tile step.  At the top of iteration kt: tile kt has
+    // landed for every wave and every wave is done with tile kt-1, whose LDS
+    // stage then receives tile kt+1.
+    issue_tile(0, 0);
+    int kt = 0;
+    for (; kt < n_full; ++kt) {
+        const int stg = kt & 1;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (kt + 1 < n_kt) load_tile(kt + 1);
-
-        const int key0 = kt * BC;
-        // nothing to do for a wave whose rows are all padding, or (causal)
-        // whose queries all precede the tile
-        if (q_w0 >= Nq || (CAUSAL && key0 > q_w0 + 31)) continue;
-
-        const u32x4* ks = smem + (st * 2 + 0) * TILE_CH;
-        const lds_char* vs = (const lds_char*)(smem + (st * 2 + 1) * TILE_CH);
-
-        // ---- S^T = K Q^T for the tile: sacc[kb][r] = S[q][key0 + kb*32 + (r/4)*8 + hi*4 + r%4]
-        f32x16 sacc[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-            const int row = kb * 32 + col;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const u32x4 kx = ks[row * DCH + k_swz<D>(row, 2 * kk + hi)];
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, kx), qreg[kk], sacc[kb], 0, 0, 0);
-            }
-        }
-
-        // ---- mask (ragged tail, causal diagonal), row max
-        const bool need_mask = (key0 + BC > Nk) || (CAUSAL && key0 + BC - 1 > q_w0);
-        float mx = -INFINITY;
-        if (need_mask) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = key0 + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-                    const bool ok = key < Nk && (!CAUSAL || key <= q);
-                    sacc[kb][r] = ok ? sacc[kb][r] : -INFINITY;
-                    mx = fmaxf(mx, sacc[kb][r]);
-                }
-        } else {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-        }
-        mx = fmaxf(mx, xor32(mx));
-        const float mt2 = (mx == -INFINITY) ? -INFINITY : mx * sl2;
-
-        // ---- max update and rescale (skipped by the whole wave when no row moved)
-        const bool move = mt2 > m_run;
-        const float m_new = move ? mt2 : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 1 when not moved, 0 first time
-        if (__builtin_amdgcn_ballot_w64(move)) {
-            l_run *= alpha;
-            lt_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        }
-        m_run = m_new;
-
-        // ---- P = exp2(S*scale*log2e - m), row sums, pack to bf16
-        const float nm = -m_new;
-        unsigned pk[KB][8];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            float pv[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], sl2, nm));
-                if (need_mask) e = (sacc[kb][r] == -INFINITY) ? 0.f : e;
-                pv[r] = e;
-                l_run += e;
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                pk[kb][j] = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
-                lt_run = add_bf16x2(pk[kb][j], lt_run);
-            }
-        }
-
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const bf16x8 pb = __builtin_bit_cast(
-                    bf16x8, (u32x4){pk[kb][4 * u + 0], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]});
-                const int r0 = kb * 32 + 16 * u + tr_row;       // keys for slots 0..3
-                const int r1 = r0 + 8;                          // keys for slots 4..7
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const int dd = db * 32 + tr_dd;
-                    const int c = dd >> 3, w = (dd & 7) * 2;
-                    const lds_i16x4* a0 = (const lds_i16x4*)(vs + r0 * (D * 2) + v_swz<D>(r0, c) * 16 + w);
-                    const lds_i16x4* a1 = (const lds_i16x4*)(vs + r1 * (D * 2) + v_swz<D>(r1, c) * 16 + w);
-                    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
-                    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a1);
-                    const bf16x8 va = __builtin_bit_cast(
-                        bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[db], 0, 0, 0);
-                }
-            }
-        }
+        if (kt + 1 < n_kt) issue_tile(kt + 1, stg ^ 1);
+        tile_step<D, false, CAUSAL>(st, qreg, smem + (stg * 2 + 0) * TILE_CH, lds + (stg * 2 + 1) * TILE_CH * 16,
+                                    kt * BC, q, Nk, sl2, col, hi, tr_row, tr_dd);
+    }
+    for (; kt < n_kt; ++kt) {
+        const int stg = kt & 1;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (kt + 1 < n_kt) issue_tile(kt + 1, stg ^ 1);
+        if (kt < n_kt_wave)
+            tile_step<D, true, CAUSAL>(st, qreg, smem + (stg * 2 + 0) * TILE_CH, lds + (stg * 2 + 1) * TILE_CH * 16,
+                                       kt * BC, q, Nk, sl2, col, hi, tr_row, tr_dd);
     }
 
     // ---- epilogue
-    const float l_tot = l_run + xor32(l_run);
-    const float lt_tot = lt_run + xor32(lt_run);
+    const float l_tot = st.l + xor32(st.l);
+    const float lt_tot = st.lt + xor32(st.lt);
     if (q < Nq) {
         const float inv = 1.0f / lt_tot;
         char* obase = (char*)p.o;
@@ -374,8 +407,8 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int dd = db * 32 + g * 8 + hi * 4;
-                const float o0 = oacc[db][4 * g + 0] * inv, o1 = oacc[db][4 * g + 1] * inv;
-                const float o2 = oacc[db][4 * g + 2] * inv, o3 = oacc[db][4 * g + 3] * inv;
+                const float o0 = st.oacc[db][4 * g + 0] * inv, o1 = st.oacc[db][4 * g + 1] * inv;
+                const float o2 = st.oacc[db][4 * g + 2] * inv, o3 = st.oacc[db][4 * g + 3] * inv;
                 if constexpr (OUT_BF16) {
                     u32x2 w = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
                     *(u32x2*)(obase + (orow + dd) * 2) = w;
@@ -384,7 +417,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_bf16_kernel(FwdParams p) {
                 }
             }
         if (p.lse && hi == 0)
-            p.lse[(long long)bh * Nq + q] = (m_run + __log2f(l_tot)) * kLn2;
+            p.lse[(long long)bh * Nq + q] = (st.m + __log2f(l_tot)) * kLn2;
     }
 }
 
@@ -533,7 +566,10 @@ using namespace fa355;
 
 namespace {
 
-constexpr int kWavesBf16 = 4;   // queries per workgroup = 32 * waves
+#ifndef FA_WAVES_BF16
+#define FA_WAVES_BF16 8
+#endif
+constexpr int kWavesBf16 = FA_WAVES_BF16;   // queries per workgroup = 32 * waves
 constexpr int kWavesF32 = 4;
 
 template <int D, bool CAUSAL, bool OUT_BF16>
