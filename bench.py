@@ -111,11 +111,14 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="selfattn_b4h32n8k")
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes 3 times (the "
+                         "reference for scaling HBM counters), then exit")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -131,6 +134,15 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py: no GPU", file=sys.stderr)
         return 1
+    if args.calibrate_copy:
+        n = args.calibrate_copy // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n * 4}), flush=True)
+        return 0
     w = I.WORKLOADS[args.workload]
     fa.load()
     print(f"bench: generating inputs for {w.name}", file=sys.stderr, flush=True)
