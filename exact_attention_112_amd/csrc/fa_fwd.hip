@@ -23,24 +23,23 @@
 //   * one workgroup = NW wavefronts x 32 queries; grid over (batch*head,
 //     query tile), remapped so the tiles of one head run on one XCD (L2);
 //   * Q fragment held in VGPRs for the whole loop;
-//   * K and V tiles of 64 keys staged HBM -> VGPR -> LDS with 16-byte loads,
-//     double buffered (tile j+1 is in flight while tile j is computed), LDS
-//     rows XOR-swizzled in 16-byte units against bank conflicts;
+//   * K and V tiles of 64 keys go HBM -> LDS directly (global_load_lds, 16
+//     bytes a lane), two LDS stages each, rows XOR-swizzled in 16-byte units
+//     against bank conflicts;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (fp32 accumulate): a lane owns
-//     one query column, so the row max / row sum are in-lane plus one exchange
-//     between the two 32-lane halves;
+//     one query column, so the row max / row sum are in-lane plus one swap of
+//     the two 32-lane halves (v_permlane32_swap);
+//   * software pipeline inside each wave: while the matrix core computes the
+//     scores of key tile j+1, the vector ALU turns the scores of tile j into
+//     probabilities; while it computes O += P_j V_j, the vector ALU takes the
+//     row max of tile j+1.  Two waves per SIMD fill each other's gaps;
 //   * P stays in registers: rounded to bf16 (RNE, v_cvt_pk_bf16_f32) and fed as
 //     the B operand of O^T = V^T P^T; V^T fragments come straight from the
 //     row-major LDS tile through ds_read_b64_tr_b16 (transposing LDS read);
 //   * exp2 with scale*log2(e) folded into one FMA; the running max follows
-//     every increase, so the row's dominant key always gets p = 1 exactly and
-//     its bf16 rounding is exact;
-//   * two row sums: l over the fp32 probabilities (for the log-sum-exp) and
-//     lt over the bf16-rounded probabilities that the P V product actually
-//     used (v_dot2c_f32_bf16 against (1,1)); O = acc / lt is then an exact
-//     convex combination of V rows, which removes the bias of the rounding
-//     when one key dominates;
-//   * epilogue: O = acc / lt in fp32 (or bf16), LSE = (m2 + log2 l) * ln 2.
+//     every increase, so the row's largest score so far always gets p = 1
+//     exactly and its bf16 rounding is exact;
+//   * epilogue: O = acc / l in fp32 (or bf16), LSE = (m2 + log2 l) * ln 2.
 // A plain fp32 kernel (v_mfma_f32_32x32x2f32, P kept in fp32) serves fp32
 // inputs; there the running max moves only when a tile's max exceeds it by
 // more than 2^8 (exact: numerator and denominator share the stale max), which
@@ -54,7 +53,6 @@
 namespace fa355 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -63,6 +61,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -131,111 +130,127 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(unsigned, r);
 }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
-
-// acc + a.lo + a.hi for a packed pair of bf16 (exact products by 1.0, fp32 sum)
-__device__ __forceinline__ float add_bf16x2(unsigned a, float acc) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), one, acc, false);
+// x of this lane and x of the lane 32 apart, combined (every lane gets the
+// result for its pair).  v_permlane32_swap(a, b) exchanges lanes 32..63 of a
+// with lanes 0..31 of b; with a = b = x the two registers then hold x's low
+// half and x's high half, each in both halves.  Written as inline assembly:
+// the compiler's builtin for it returns the first register twice.  The
+// s_nop covers the VALU-write -> permlane-read hazard.
+__device__ __forceinline__ void swap_halves(float x, float& a, float& b) {
+    unsigned u = __builtin_bit_cast(unsigned, x), w = u;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(u), "+v"(w));
+    a = __builtin_bit_cast(float, u);
+    b = __builtin_bit_cast(float, w);
 }
+__device__ __forceinline__ float pair_max(float x) {
+    float a, b;
+    swap_halves(x, a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    float a, b;
+    swap_halves(x, a, b);
+    return a + b;
+}
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 // ---------------------------------------------------------------------------
 // bf16 kernel
 //
 // D: head dim (64 or 128).  NW: waves per workgroup (32 queries each).
 // OUT_BF16: write O as bf16 instead of fp32.
+//
+// Register layout of one wave (32 queries; lane = (col, hi), col = lane % 32
+// is the query, hi = lane / 32 picks half of each 8-key group):
+//   S^T tile (two f32x16 per 64 keys): s[kb][r] = score of key
+//     kb*32 + (r/4)*8 + hi*4 + r%4 against query col;
+//   O^T accumulator: oacc[db][r] = O[col][db*32 + (r/4)*8 + hi*4 + r%4].
 
-// Per-wave state of the online softmax for its 32 queries (one per lane; the
-// two 32-lane halves hold the same query and split its keys).
 template <int D>
 struct RowState {
-    f32x16 oacc[D / 32];   // O^T accumulator: oacc[db][r] = O[q][db*32 + (r/4)*8 + hi*4 + r%4]
-    float m;               // running max of scale*log2(e)*s
-    float l;               // partial sum of fp32 P over this lane's keys
-    float lt;              // partial sum of bf16-rounded P
+    f32x16 oacc[D / 32];
+    float m;          // running max of scale*log2(e)*s (same in both halves)
+    float l0, l1;     // two partial sums of P over this lane's keys
 };
 
-// One 64-key tile for one wave: S^T = K Q^T, (mask), online softmax, O^T += V^T P^T.
-//   ks:   K tile in LDS, [64][D/8] 16-byte chunks, swizzled by k_swz
-//   vs:   V tile in LDS, same shape, swizzled by v_swz (byte pointer)
-//   key0: first key of the tile; q: this lane's query (masking only)
-template <int D, bool MASK, bool CAUSAL>
-__device__ __forceinline__ void tile_step(RowState<D>& st, const bf16x8 (&qreg)[D / 16],
-                                          const u32x4* __restrict__ ks, const lds_char* vs,
-                                          int key0, int q, int Nk, float sl2,
-                                          int col, int hi, int tr_row, int tr_dd) {
-    constexpr int DCH = D / 8, KK = D / 16, DB = D / 32;
-
-    // ---- S^T for the two 32-key halves of the tile
-    f32x16 sacc[2];
+// S^T = K Q^T for one 64-key tile: 2 x D/16 MFMAs.
+template <int D>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const bf16x8 (&qreg)[D / 16],
+                                        const u32x4* __restrict__ ks, int col, int hi) {
+    constexpr int DCH = D / 8, KK = D / 16;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-        const int row = kb * 32 + col;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
+        for (int kb = 0; kb < 2; ++kb) {
+            const int row = kb * 32 + col;
             const u32x4 kx = ks[row * DCH + k_swz<D>(row, 2 * kk + hi)];
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qreg[kk],
-                                                               sacc[kb], 0, 0, 0);
+            const f32x16 c = kk == 0 ? f32x16{} : s[kb];
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qreg[kk], c,
+                                                            0, 0, 0);
         }
     }
+}
 
-    // ---- mask, row max (in-lane, then across the two halves)
-    if constexpr (MASK) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = key0 + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-                const bool ok = key < Nk && (!CAUSAL || key <= q);
-                sacc[kb][r] = ok ? sacc[kb][r] : -INFINITY;
-            }
-    }
-    float mx = sacc[0][0];
+// Keys >= Nk and (causal) keys after the lane's query -> -inf.
+template <bool CAUSAL>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int key0, int q, int Nk, int hi) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, xor32(mx));
-    // scale >= 0, so the max of the scaled scores is the scaled max
-    const float mt2 = (MASK && mx == -INFINITY) ? -INFINITY : mx * sl2;
+        for (int r = 0; r < 16; ++r) {
+            const int key = key0 + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+            const bool ok = key < Nk && (!CAUSAL || key <= q);
+            s[kb][r] = ok ? s[kb][r] : -INFINITY;
+        }
+}
 
-    // ---- move the max and rescale (skipped by the whole wave when no row moved)
-    const bool move = mt2 > st.m;
-    const float m_new = move ? mt2 : st.m;
-    if (__builtin_amdgcn_ballot_w64(move)) {
-        const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // 1 if not moved, 0 the first time
-        st.l *= alpha;
-        st.lt *= alpha;
+// Row max of the tile, scaled to log2 units (scale >= 0, so the max of the
+// scaled scores is the scaled max); -inf if every key of the row is masked.
+template <bool MASK>
+__device__ __forceinline__ float tile_max_scaled(const f32x16 (&s)[2], float sl2) {
+    float a = fmaxf(s[0][0], s[0][1]), b = fmaxf(s[0][2], s[0][3]);
+    float c = fmaxf(s[1][0], s[1][1]), d = fmaxf(s[1][2], s[1][3]);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
-        st.m = m_new;
+    for (int r = 4; r < 16; r += 2) {
+        a = fmaxf(a, s[0][r]);
+        b = fmaxf(b, s[0][r + 1]);
+        c = fmaxf(c, s[1][r]);
+        d = fmaxf(d, s[1][r + 1]);
     }
+    const float mx = pair_max(fmaxf(fmaxf(a, b), fmaxf(c, d)));
+    if constexpr (MASK) return mx == -INFINITY ? -INFINITY : mx * sl2;
+    else return mx * sl2;
+}
 
-    // ---- P = exp2(s*scale*log2e - m); sums; bf16 pack
-    const float nm = -st.m;
-    unsigned pk[2][8];
+// P = exp2(s*scale*log2e - m), accumulated into the two row-sum chains and
+// packed to bf16 pairs (the B operand of the P V product).
+template <bool MASK>
+__device__ __forceinline__ void tile_exp(const f32x16 (&s)[2], float m, float sl2, unsigned (&pk)[2][8],
+                                         float& l0, float& l1) {
+    const float nm = -m;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][2 * j], sl2, nm));
-            float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][2 * j + 1], sl2, nm));
+            float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * j], sl2, nm));
+            float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * j + 1], sl2, nm));
             if constexpr (MASK) {   // -inf * 0 (scale 0) would be NaN: force masked keys to 0
-                e0 = sacc[kb][2 * j] == -INFINITY ? 0.f : e0;
-                e1 = sacc[kb][2 * j + 1] == -INFINITY ? 0.f : e1;
+                e0 = s[kb][2 * j] == -INFINITY ? 0.f : e0;
+                e1 = s[kb][2 * j + 1] == -INFINITY ? 0.f : e1;
             }
-            st.l += e0;
-            st.l += e1;
+            l0 += e0;
+            l1 += e1;
             pk[kb][j] = pack_bf16x2(e0, e1);
-            st.lt = add_bf16x2(pk[kb][j], st.lt);
         }
-    }
+}
 
-    // ---- O^T += V^T P^T
+// O^T += V^T P^T for one 64-key tile: 4 x D/32 MFMAs.  The lane's P slots
+// 0..3 of 16-key group u hold keys 16u + hi*4 + 0..3 and slots 4..7 keys
+// 16u + 8 + hi*4 + 0..3; the V^T fragment is read for the same keys.
+template <int D>
+__device__ __forceinline__ void pv_tile(f32x16 (&oacc)[D / 32], const unsigned (&pk)[2][8],
+                                        const lds_char* vs, int tr_row, int tr_dd) {
+    constexpr int DB = D / 32;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -253,20 +268,94 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, const bf16x8 (&qreg)[
                 const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_i16x4*)(vs + r1 * (D * 2) + v_swz<D>(r1, c) * 16 + w));
                 const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-                st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, st.oacc[db], 0, 0, 0);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[db], 0, 0, 0);
             }
         }
     }
 }
 
+// Move the running max to include a new tile whose scaled row max is mt2.
+// The rescale by alpha = exp2(m_old - m_new) is skipped by the whole wave when
+// no row's max moved (alpha would be 1 for every lane).
+template <int D>
+__device__ __forceinline__ void update_max(RowState<D>& st, float mt2) {
+    const bool move = mt2 > st.m;
+    if (__builtin_amdgcn_ballot_w64(move)) {
+        const float m_new = move ? mt2 : st.m;
+        const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+        st.l0 *= alpha;
+        st.l1 *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
+        st.m = m_new;
+    }
+}
+
+// Instruction order of one pipelined step (one scheduling region), written
+// for the compiler's scheduler: phase A interleaves the scores of tile j+1
+// (one K fragment read and one MFMA at a time) with the exponentials of tile
+// j; phase B interleaves O += P V (two V^T fragment reads per MFMA) with the
+// row max of tile j+1.  LDS reads run two MFMAs ahead of their use.
+enum : unsigned { kSgVALU = 0x2, kSgMFMA = 0x8, kSgDSRead = 0x100, kSgTrans = 0x400 };
+template <int D>
+__device__ __forceinline__ void schedule_step() {
+    constexpr int NA = 2 * (D / 16);   // QK MFMAs
+    constexpr int NB = 4 * (D / 32);   // PV MFMAs
+    constexpr int VA = 80 / NA, TA = 32 / NA;
+    __builtin_amdgcn_sched_group_barrier(kSgDSRead, 2, 0);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgVALU, VA, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgTrans, TA, 0);
+        if (i + 2 < NA) __builtin_amdgcn_sched_group_barrier(kSgDSRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgDSRead, 4, 0);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgVALU, 2, 0);
+        if (i + 2 < NB) __builtin_amdgcn_sched_group_barrier(kSgDSRead, 2, 0);
+    }
+}
+
+// One pipelined step of a wave: probabilities of tile j (scores in s_cur,
+// the running max already includes tile j) and O += P_j V_j, overlapped with
+// the scores of tile j+1 (into s_nxt) and their row max.
+//   ks_nxt: K tile j+1 in LDS; vs_cur: V tile j in LDS (bytes)
+template <int D, bool CAUSAL, bool MASK_CUR, bool MASK_NXT, bool HAS_NXT>
+__device__ __forceinline__ void wave_step(RowState<D>& st, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+                                          const bf16x8 (&qreg)[D / 16], const u32x4* ks_nxt,
+                                          const lds_char* vs_cur, int key0_nxt, int q, int Nk, float sl2,
+                                          int col, int hi, int tr_row, int tr_dd) {
+    unsigned pk[2][8];
+    if constexpr (HAS_NXT) qk_tile<D>(s_nxt, qreg, ks_nxt, col, hi);
+    tile_exp<MASK_CUR>(s_cur, st.m, sl2, pk, st.l0, st.l1);
+    pv_tile<D>(st.oacc, pk, vs_cur, tr_row, tr_dd);
+    if constexpr (HAS_NXT) {
+        if constexpr (MASK_NXT) mask_tile<CAUSAL>(s_nxt, key0_nxt, q, Nk, hi);
+        const float mt2 = tile_max_scaled<MASK_NXT>(s_nxt, sl2);
+        schedule_step<D>();
+        update_max(st, mt2);
+    }
+}
+
+// One 16-byte-per-lane buffer load into LDS: lane i of the wave writes the
+// 16 bytes at rsrc + voff to lds_dst + 16*i.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, lds_char* lds_dst, unsigned voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_dst, 16, voff, 0, 0, 0);
+}
+
 template <int D, int NW>
 struct Bf16Cfg {
     static constexpr int BC = 64;                 // keys per tile
-    static constexpr int NT = NW * 64;            // threads per workgroup
     static constexpr int BR = NW * 32;            // queries per workgroup
     static constexpr int DCH = D / 8;             // 16-byte chunks per row
     static constexpr int TILE_CH = BC * DCH;      // chunks per K (or V) tile
-    static constexpr int LD_PER_WAVE = TILE_CH / 64 / NW;   // direct-to-LDS loads per wave per operand
+    static constexpr int TILE_BYTES = TILE_CH * 16;
+    static constexpr int LPW = TILE_CH / 64 / NW; // direct-to-LDS loads per wave per operand
     static_assert(TILE_CH % (64 * NW) == 0, "tile must split evenly over the waves");
 };
 
@@ -274,11 +363,11 @@ template <int D, int NW, bool CAUSAL, bool OUT_BF16>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_kernel(FwdParams p) {
     using C = Bf16Cfg<D, NW>;
-    constexpr int BC = C::BC, BR = C::BR, DCH = C::DCH, TILE_CH = C::TILE_CH;
-    constexpr int KK = D / 16, DB = D / 32;
+    constexpr int BC = C::BC, BR = C::BR, DCH = C::DCH, TILE_CH = C::TILE_CH, TB = C::TILE_BYTES;
+    constexpr int LPW = C::LPW, KK = D / 16, DB = D / 32;
 
-    // [stage][K|V][TILE_CH] 16-byte chunks
-    __shared__ u32x4 smem[2 * 2 * TILE_CH];
+    // K stages 0, 1 then V stages 0, 1; [TILE_CH] 16-byte chunks each
+    __shared__ u32x4 smem[4 * TILE_CH];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -297,13 +386,14 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     const int Nq = p.Nq, Nk = p.Nk;
 
     const __bf16* qbase = (const __bf16*)p.q + (long long)b * p.q_sb + (long long)h * p.q_sh;
-    const __bf16* kbase = (const __bf16*)p.k + (long long)b * p.k_sb + (long long)h * p.k_sh;
-    const __bf16* vbase = (const __bf16*)p.v + (long long)b * p.k_sb + (long long)h * p.k_sh;
+    const char* kbase = (const char*)((const __bf16*)p.k + (long long)b * p.k_sb + (long long)h * p.k_sh);
+    const char* vbase = (const char*)((const __bf16*)p.v + (long long)b * p.k_sb + (long long)h * p.k_sh);
+    const long long row_bytes = p.k_sn * 2;
 
-    // Keys this workgroup needs.  Tiles [0, n_full) need no mask for any wave
-    // (every key < Nk and, causal, <= the workgroup's first query); the rest
-    // go through the masked step, and a wave skips the tiles past its last
-    // query (causal) or all of them if its rows are all padding.
+    // Key tiles this workgroup needs.  Tiles [0, n_full) need no mask for any
+    // wave (every key < Nk and, causal, <= the workgroup's first query); the
+    // rest are masked, and a wave skips the tiles past its last query
+    // (causal) or all of them if its rows are all padding.
     int kv_end = Nk;
     if (CAUSAL) kv_end = min(Nk, min(q_wg0 + BR, Nq));
     const int n_kt = (kv_end + BC - 1) / BC;
@@ -325,34 +415,46 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         }
     }
 
-    // ---- direct HBM -> LDS staging.  Each wave instruction writes 64
-    // consecutive 16-byte LDS chunks; lane i of load j fills physical chunk
-    // pc = (wave*LD_PER_WAVE + j)*64 + i, i.e. row pc/DCH, swizzled chunk pc%DCH,
-    // so it fetches the logical chunk (pc%DCH) ^ swz(row).  Keys past Nk are
-    // clamped to Nk-1: their scores are masked, and V rows stay finite.
-    int ld_row[C::LD_PER_WAVE], ld_kch[C::LD_PER_WAVE], ld_vch[C::LD_PER_WAVE];
+    // ---- direct HBM -> LDS staging (buffer_load ... lds, 16 bytes a lane).
+    // Each wave instruction writes 64 consecutive 16-byte LDS chunks; lane i
+    // of load j fills physical chunk pc = (wave*LPW + j)*64 + i, i.e. row
+    // pc/DCH, swizzled chunk pc%DCH, so it fetches the logical chunk
+    // (pc%DCH) ^ swz(row) (the swizzles are XORs, their own inverse).  The
+    // buffer descriptor is rebased on each tile (scalar), the lane offsets
+    // are fixed.  A tile that runs past Nk reads row Nk-1 in place of the
+    // missing rows: their scores are masked, and the V rows stay finite.
+    const unsigned rb = (unsigned)row_bytes;
+    unsigned ld_koff[LPW], ld_voff[LPW];   // byte offsets inside a tile
 #pragma unroll
-    for (int j = 0; j < C::LD_PER_WAVE; ++j) {
-        const int pc = (wave * C::LD_PER_WAVE + j) * 64 + lane;
-        const int row = pc / DCH, ch = pc - (pc / DCH) * DCH;
-        ld_row[j] = row;
-        ld_kch[j] = k_swz<D>(row, ch);   // XOR swizzles are their own inverse
-        ld_vch[j] = v_swz<D>(row, ch);
+    for (int j = 0; j < LPW; ++j) {
+        const int pc = (wave * LPW + j) * 64 + lane;
+        const int row = pc / DCH, ch = pc % DCH;
+        ld_koff[j] = row * rb + k_swz<D>(row, ch) * 16;
+        ld_voff[j] = row * rb + v_swz<D>(row, ch) * 16;
     }
     lds_char* const lds = (lds_char*)smem;
-    auto issue_tile = [&](int kt, int stg) {
-        lds_char* kdst = lds + (stg * 2 + 0) * TILE_CH * 16 + wave * C::LD_PER_WAVE * 1024;
-        lds_char* vdst = lds + (stg * 2 + 1) * TILE_CH * 16 + wave * C::LD_PER_WAVE * 1024;
+    auto issue = [&](const char* base, const unsigned (&off)[LPW], int t, lds_char* stage) {
+        lds_char* dst = stage + wave * LPW * 1024;
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(base + (long long)t * BC * row_bytes),
+                                                            (short)0, (int)(BC * rb), 0x00020000);
+        const int nvalid = Nk - t * BC;   // rows of this tile inside the sequence
+        if (nvalid >= BC) {
 #pragma unroll
-        for (int j = 0; j < C::LD_PER_WAVE; ++j) {
-            const int key = min(kt * BC + ld_row[j], Nk - 1);
-            const long long roff = (long long)key * p.k_sn;
-            __builtin_amdgcn_global_load_lds((const void*)(kbase + roff + ld_kch[j] * 8),
-                                             (__attribute__((address_space(3))) void*)(kdst + j * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(vbase + roff + ld_vch[j] * 8),
-                                             (__attribute__((address_space(3))) void*)(vdst + j * 1024), 16, 0, 0);
+            for (int j = 0; j < LPW; ++j)
+                load_lds16(rsrc, dst + j * 1024, off[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < LPW; ++j) {
+                const int row = ((wave * LPW + j) * 64 + lane) / DCH;
+                const unsigned o = off[j] - (unsigned)(row - min(row, nvalid - 1)) * rb;
+                load_lds16(rsrc, dst + j * 1024, o);
+            }
         }
     };
+    auto k_stage = [&](int t) { return lds + (t & 1) * TB; };
+    auto v_stage = [&](int t) { return lds + (2 + (t & 1)) * TB; };
+    auto issue_k = [&](int t) { issue(kbase, ld_koff, t, k_stage(t)); };
+    auto issue_v = [&](int t) { issue(vbase, ld_voff, t, v_stage(t)); };
 
     RowState<D> st;
 #pragma unroll
@@ -360,8 +462,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) st.oacc[db][r] = 0.f;
     st.m = -INFINITY;
-    st.l = 0.f;
-    st.lt = 0.f;
+    st.l0 = 0.f;
+    st.l1 = 0.f;
     const float sl2 = p.scale_log2;
 
     // V^T fragment addressing for ds_read_b64_tr_b16: within each 16-lane
@@ -371,35 +473,65 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     const int tr_row = hi * 4 + (ti >> 2);            // key offset inside an 8-key group
     const int tr_dd = 16 * (tg & 1) + 4 * (ti & 3);   // d offset inside a 32-wide d block
 
-    // Two loops with the same barrier structure, so the unmasked one has no
-    // branch around its tile step.  At the top of iteration kt: tile kt has
-    // landed for every wave and every wave is done with tile kt-1, whose LDS
-    // stage then receives tile kt+1.
-    issue_tile(0, 0);
-    int kt = 0;
-    for (; kt < n_full; ++kt) {
-        const int stg = kt & 1;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (kt + 1 < n_kt) issue_tile(kt + 1, stg ^ 1);
-        tile_step<D, false, CAUSAL>(st, qreg, smem + (stg * 2 + 0) * TILE_CH, lds + (stg * 2 + 1) * TILE_CH * 16,
-                                    kt * BC, q, Nk, sl2, col, hi, tr_row, tr_dd);
+    // Pipeline.  K tile t lives in K stage t%2, V tile t in V stage t%2.
+    // Step j (top: K tile j+1 and V tile j have landed for every wave, and
+    // every wave is done with step j-1) first refills the stages step j-1
+    // read: K tile j+2 and V tile j+1; then computes P_j, O += P_j V_j and
+    // the scores of tile j+1.
+    issue_k(0);
+    issue_v(0);
+    if (n_kt > 1) issue_k(1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // Scores of tile 0.  Every row (padding rows included: their Q is zero)
+    // sees key 0, so the first max is finite.
+    f32x16 sa[2], sb[2];   // scores of the current / next tile (roles alternate)
+    qk_tile<D>(sa, qreg, (const u32x4*)k_stage(0), col, hi);
+    if (n_full > 0) {
+        st.m = tile_max_scaled<false>(sa, sl2);
+    } else {
+        mask_tile<CAUSAL>(sa, 0, q, Nk, hi);
+        st.m = tile_max_scaled<true>(sa, sl2);
     }
-    for (; kt < n_kt; ++kt) {
-        const int stg = kt & 1;
+
+    auto top = [&](int j) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (kt + 1 < n_kt) issue_tile(kt + 1, stg ^ 1);
-        if (kt < n_kt_wave)
-            tile_step<D, true, CAUSAL>(st, qreg, smem + (stg * 2 + 0) * TILE_CH, lds + (stg * 2 + 1) * TILE_CH * 16,
-                                       kt * BC, q, Nk, sl2, col, hi, tr_row, tr_dd);
+        if (j + 2 < n_kt) issue_k(j + 2);
+        if (j + 1 < n_kt) issue_v(j + 1);
+    };
+
+    // Steps whose tiles j and j+1 are both unmasked, two at a time so the
+    // score buffers swap roles without copies.
+    int j = 0;
+    for (; j + 2 < n_full; j += 2) {
+        top(j);
+        wave_step<D, CAUSAL, false, false, true>(st, sa, sb, qreg, (const u32x4*)k_stage(j + 1), v_stage(j),
+                                                 (j + 1) * BC, q, Nk, sl2, col, hi, tr_row, tr_dd);
+        top(j + 1);
+        wave_step<D, CAUSAL, false, false, true>(st, sb, sa, qreg, (const u32x4*)k_stage(j + 2), v_stage(j + 1),
+                                                 (j + 2) * BC, q, Nk, sl2, col, hi, tr_row, tr_dd);
+    }
+    // The remaining steps (at most a few): masks on, per-wave skips.
+    for (; j < n_kt; ++j) {
+        top(j);
+        if (j < n_kt_wave) {
+            if (j + 1 < n_kt_wave)
+                wave_step<D, CAUSAL, true, true, true>(st, sa, sb, qreg, (const u32x4*)k_stage(j + 1), v_stage(j),
+                                                       (j + 1) * BC, q, Nk, sl2, col, hi, tr_row, tr_dd);
+            else
+                wave_step<D, CAUSAL, true, true, false>(st, sa, sb, qreg, nullptr, v_stage(j), 0, q, Nk, sl2, col,
+                                                        hi, tr_row, tr_dd);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
+        }
     }
 
     // ---- epilogue
-    const float l_tot = st.l + xor32(st.l);
-    const float lt_tot = st.lt + xor32(st.lt);
+    const float l_tot = pair_sum(st.l0 + st.l1);
     if (q < Nq) {
-        const float inv = 1.0f / lt_tot;
+        const float inv = 1.0f / l_tot;
         char* obase = (char*)p.o;
         const long long orow = (long long)b * p.q_sb + (long long)h * p.q_sh + (long long)q * p.q_sn;
 #pragma unroll
@@ -420,6 +552,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
             p.lse[(long long)bh * Nq + q] = (st.m + __log2f(l_tot)) * kLn2;
     }
 }
+
 
 // ---------------------------------------------------------------------------
 // fp32 kernel: same method, v_mfma_f32_32x32x2f32, P kept in fp32, one
@@ -620,6 +753,9 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     const long long n_qtiles = ((long long)Nq + rows_per_wg - 1) / rows_per_wg;
     const long long grid = n_qtiles * B * H;
     if ((long long)B * H > INT32_MAX || grid > INT32_MAX) return FA_ERR_UNSUPPORTED;
+    // the bf16 kernel addresses a 64-row key tile with 32-bit byte offsets
+    const long long kv_row_bytes = (layout == FA_BSND ? (long long)H * d : (long long)d) * 2;
+    if (in_dtype == FA_BF16 && 64 * kv_row_bytes > INT32_MAX) return FA_ERR_UNSUPPORTED;
 
     if (scale < 0.f) scale = 1.0f / sqrtf((float)d);
 
