@@ -152,7 +152,6 @@ __device__ __forceinline__ float pair_sum(float x) {
     swap_halves(x, a, b);
     return a + b;
 }
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 // ---------------------------------------------------------------------------
 // bf16 kernel
@@ -191,40 +190,36 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const bf16x8 (&qreg)[D /
     }
 }
 
-// Keys >= Nk and (causal) keys after the lane's query -> -inf.
+// Keys >= Nk and (causal) keys after the lane's query -> -inf.  The lane's
+// key for slot (kb, r) is key0 + hi*4 + [kb*32 + (r/4)*8 + r%4]; it is visible
+// iff the bracket is <= lim.
 template <bool CAUSAL>
 __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int key0, int q, int Nk, int hi) {
+    const int lim = (CAUSAL ? min(Nk - 1, q) : Nk - 1) - (key0 + hi * 4);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-            const bool ok = key < Nk && (!CAUSAL || key <= q);
-            s[kb][r] = ok ? s[kb][r] : -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+            s[kb][r] = (kb * 32 + (r >> 2) * 8 + (r & 3)) <= lim ? s[kb][r] : -INFINITY;
 }
 
-// Row max of the tile, scaled to log2 units (scale >= 0, so the max of the
-// scaled scores is the scaled max); -inf if every key of the row is masked.
-template <bool MASK>
+// Row max of the tile, scaled to log2 units (the scale is > 0, so the max of
+// the scaled scores is the scaled max); -inf if every key of the row is masked.
 __device__ __forceinline__ float tile_max_scaled(const f32x16 (&s)[2], float sl2) {
-    float a = fmaxf(s[0][0], s[0][1]), b = fmaxf(s[0][2], s[0][3]);
-    float c = fmaxf(s[1][0], s[1][1]), d = fmaxf(s[1][2], s[1][3]);
+    // two chains of 3-input maxes (v_max3_f32), 8 each
+    float a = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+    float b = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
 #pragma unroll
-    for (int r = 4; r < 16; r += 2) {
-        a = fmaxf(a, s[0][r]);
-        b = fmaxf(b, s[0][r + 1]);
-        c = fmaxf(c, s[1][r]);
-        d = fmaxf(d, s[1][r + 1]);
+    for (int r = 3; r < 15; r += 2) {
+        a = fmaxf(fmaxf(a, s[0][r]), s[0][r + 1]);
+        b = fmaxf(fmaxf(b, s[1][r]), s[1][r + 1]);
     }
-    const float mx = pair_max(fmaxf(fmaxf(a, b), fmaxf(c, d)));
-    if constexpr (MASK) return mx == -INFINITY ? -INFINITY : mx * sl2;
-    else return mx * sl2;
+    return pair_max(fmaxf(fmaxf(a, s[0][15]), fmaxf(b, s[1][15]))) * sl2;
 }
 
 // P = exp2(s*scale*log2e - m), accumulated into the two row-sum chains and
-// packed to bf16 pairs (the B operand of the P V product).
-template <bool MASK>
+// packed to bf16 pairs (the B operand of the P V product).  Masked scores are
+// -inf and give exactly 0 (the scale is > 0).
 __device__ __forceinline__ void tile_exp(const f32x16 (&s)[2], float m, float sl2, unsigned (&pk)[2][8],
                                          float& l0, float& l1) {
     const float nm = -m;
@@ -232,12 +227,8 @@ __device__ __forceinline__ void tile_exp(const f32x16 (&s)[2], float m, float sl
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * j], sl2, nm));
-            float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * j + 1], sl2, nm));
-            if constexpr (MASK) {   // -inf * 0 (scale 0) would be NaN: force masked keys to 0
-                e0 = s[kb][2 * j] == -INFINITY ? 0.f : e0;
-                e1 = s[kb][2 * j + 1] == -INFINITY ? 0.f : e1;
-            }
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * j], sl2, nm));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * j + 1], sl2, nm));
             l0 += e0;
             l1 += e1;
             pk[kb][j] = pack_bf16x2(e0, e1);
@@ -325,18 +316,18 @@ __device__ __forceinline__ void schedule_step() {
 // the running max already includes tile j) and O += P_j V_j, overlapped with
 // the scores of tile j+1 (into s_nxt) and their row max.
 //   ks_nxt: K tile j+1 in LDS; vs_cur: V tile j in LDS (bytes)
-template <int D, bool CAUSAL, bool MASK_CUR, bool MASK_NXT, bool HAS_NXT>
+template <int D, bool CAUSAL, bool MASK_NXT, bool HAS_NXT>
 __device__ __forceinline__ void wave_step(RowState<D>& st, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
                                           const bf16x8 (&qreg)[D / 16], const u32x4* ks_nxt,
                                           const lds_char* vs_cur, int key0_nxt, int q, int Nk, float sl2,
                                           int col, int hi, int tr_row, int tr_dd) {
     unsigned pk[2][8];
     if constexpr (HAS_NXT) qk_tile<D>(s_nxt, qreg, ks_nxt, col, hi);
-    tile_exp<MASK_CUR>(s_cur, st.m, sl2, pk, st.l0, st.l1);
+    tile_exp(s_cur, st.m, sl2, pk, st.l0, st.l1);
     pv_tile<D>(st.oacc, pk, vs_cur, tr_row, tr_dd);
     if constexpr (HAS_NXT) {
         if constexpr (MASK_NXT) mask_tile<CAUSAL>(s_nxt, key0_nxt, q, Nk, hi);
-        const float mt2 = tile_max_scaled<MASK_NXT>(s_nxt, sl2);
+        const float mt2 = tile_max_scaled(s_nxt, sl2);
         schedule_step<D>();
         update_max(st, mt2);
     }
@@ -346,6 +337,36 @@ __device__ __forceinline__ void wave_step(RowState<D>& st, f32x16 (&s_cur)[2], f
 // 16 bytes at rsrc + voff to lds_dst + 16*i.
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, lds_char* lds_dst, unsigned voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_dst, 16, voff, 0, 0, 0);
+}
+
+// A wave-uniform value moved to scalar registers (the compiler cannot always
+// prove uniformity on its own; a buffer descriptor must be scalar).
+__device__ __forceinline__ unsigned long long to_sgpr(unsigned long long a) {
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// Issue the loads of one K or V tile into an LDS stage.  tile: address of the
+// tile's first row (wave-uniform); off: this lane's byte offsets inside a full
+// tile; nvalid: rows of the tile inside the sequence (rows past it re-read
+// the last valid row).
+template <int LPW, int DCH, int BC>
+__device__ __forceinline__ void issue_tile(unsigned long long tile, unsigned rb, const unsigned (&off)[LPW],
+                                           lds_char* dst, int nvalid, int wave, int lane) {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)to_sgpr(tile), (short)0, (int)(BC * rb), 0x00020000);
+    if (nvalid >= BC) {
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) load_lds16(rsrc, dst + j * 1024, off[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const int row = ((wave * LPW + j) * 64 + lane) / DCH;
+            const unsigned o = off[j] - (unsigned)(row - min(row, nvalid - 1)) * rb;
+            load_lds16(rsrc, dst + j * 1024, o);
+        }
+    }
 }
 
 template <int D, int NW>
@@ -369,14 +390,14 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // K stages 0, 1 then V stages 0, 1; [TILE_CH] 16-byte chunks each
     __shared__ u32x4 smem[4 * TILE_CH];
 
-    const int tid = threadIdx.x;
+    const int tid = __builtin_amdgcn_workitem_id_x();
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int col = lane & 31;
     const int hi = lane >> 5;
 
     int bh, qt;
-    tile_of_block(blockIdx.x, p.n_qtiles, p.BH, CAUSAL, bh, qt);
+    tile_of_block(__builtin_amdgcn_workgroup_id_x(), p.n_qtiles, p.BH, CAUSAL, bh, qt);
     const int b = bh / p.H;
     const int h = bh - b * p.H;
 
@@ -400,8 +421,9 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     int n_full = Nk / BC;
     if (CAUSAL) n_full = min(n_full, (q_wg0 + 1) / BC);
     n_full = min(n_full, n_kt);
-    int n_kt_wave = q_w0 < Nq ? n_kt : 0;
-    if (CAUSAL && q_w0 < Nq) n_kt_wave = min(n_kt, min(q_w0 + 31, Nq - 1) / BC + 1);
+    // (padding waves, q_w0 >= Nq, run like the others: their Q rows are zero
+    // and their results are not stored)
+    const int n_kt_wave = CAUSAL ? min(n_kt, (q_w0 + 31) / BC + 1) : n_kt;
 
     // ---- Q fragment (B operand of S^T = K Q^T): lane holds Q[q][16kk + 8hi .. +7]
     bf16x8 qreg[KK];
@@ -433,28 +455,16 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         ld_voff[j] = row * rb + v_swz<D>(row, ch) * 16;
     }
     lds_char* const lds = (lds_char*)smem;
-    auto issue = [&](const char* base, const unsigned (&off)[LPW], int t, lds_char* stage) {
-        lds_char* dst = stage + wave * LPW * 1024;
-        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(base + (long long)t * BC * row_bytes),
-                                                            (short)0, (int)(BC * rb), 0x00020000);
-        const int nvalid = Nk - t * BC;   // rows of this tile inside the sequence
-        if (nvalid >= BC) {
-#pragma unroll
-            for (int j = 0; j < LPW; ++j)
-                load_lds16(rsrc, dst + j * 1024, off[j]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < LPW; ++j) {
-                const int row = ((wave * LPW + j) * 64 + lane) / DCH;
-                const unsigned o = off[j] - (unsigned)(row - min(row, nvalid - 1)) * rb;
-                load_lds16(rsrc, dst + j * 1024, o);
-            }
-        }
-    };
-    auto k_stage = [&](int t) { return lds + (t & 1) * TB; };
-    auto v_stage = [&](int t) { return lds + (2 + (t & 1)) * TB; };
-    auto issue_k = [&](int t) { issue(kbase, ld_koff, t, k_stage(t)); };
-    auto issue_v = [&](int t) { issue(vbase, ld_voff, t, v_stage(t)); };
+    const unsigned long long kaddr = to_sgpr((unsigned long long)kbase);
+    const unsigned long long vaddr = to_sgpr((unsigned long long)vbase);
+    const unsigned long long tile_bytes = (unsigned long long)BC * (unsigned long long)row_bytes;
+    lds_char* const ldst = lds + wave * LPW * 1024;   // this wave's part of a stage
+#define FA_K_STAGE(t) (lds + ((t) & 1) * TB)
+#define FA_V_STAGE(t) (lds + (2 + ((t) & 1)) * TB)
+#define FA_ISSUE_K(t) issue_tile<LPW, DCH, BC>(kaddr + (unsigned long long)(t) * tile_bytes, rb, ld_koff, \
+                                              ldst + ((t) & 1) * TB, Nk - (t) * BC, wave, lane)
+#define FA_ISSUE_V(t) issue_tile<LPW, DCH, BC>(vaddr + (unsigned long long)(t) * tile_bytes, rb, ld_voff, \
+                                              ldst + (2 + ((t) & 1)) * TB, Nk - (t) * BC, wave, lane)
 
     RowState<D> st;
 #pragma unroll
@@ -478,55 +488,60 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // every wave is done with step j-1) first refills the stages step j-1
     // read: K tile j+2 and V tile j+1; then computes P_j, O += P_j V_j and
     // the scores of tile j+1.
-    issue_k(0);
-    issue_v(0);
-    if (n_kt > 1) issue_k(1);
+    FA_ISSUE_K(0);
+    FA_ISSUE_V(0);
+    if (n_kt > 1) FA_ISSUE_K(1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     // Scores of tile 0.  Every row (padding rows included: their Q is zero)
     // sees key 0, so the first max is finite.
     f32x16 sa[2], sb[2];   // scores of the current / next tile (roles alternate)
-    qk_tile<D>(sa, qreg, (const u32x4*)k_stage(0), col, hi);
-    if (n_full > 0) {
-        st.m = tile_max_scaled<false>(sa, sl2);
-    } else {
-        mask_tile<CAUSAL>(sa, 0, q, Nk, hi);
-        st.m = tile_max_scaled<true>(sa, sl2);
-    }
+    qk_tile<D>(sa, qreg, (const u32x4*)FA_K_STAGE(0), col, hi);
+    if (n_full == 0) mask_tile<CAUSAL>(sa, 0, q, Nk, hi);
+    st.m = tile_max_scaled(sa, sl2);
 
-    auto top = [&](int j) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (j + 2 < n_kt) issue_k(j + 2);
-        if (j + 1 < n_kt) issue_v(j + 1);
-    };
+#define FA_TOP(j)                                      \
+    do {                                               \
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); \
+        __syncthreads();                               \
+        if ((j) + 2 < n_kt) FA_ISSUE_K((j) + 2);       \
+        if ((j) + 1 < n_kt) FA_ISSUE_V((j) + 1);       \
+    } while (0)
+#define FA_KS(t) ((const u32x4*)FA_K_STAGE(t))
 
     // Steps whose tiles j and j+1 are both unmasked, two at a time so the
     // score buffers swap roles without copies.
     int j = 0;
     for (; j + 2 < n_full; j += 2) {
-        top(j);
-        wave_step<D, CAUSAL, false, false, true>(st, sa, sb, qreg, (const u32x4*)k_stage(j + 1), v_stage(j),
-                                                 (j + 1) * BC, q, Nk, sl2, col, hi, tr_row, tr_dd);
-        top(j + 1);
-        wave_step<D, CAUSAL, false, false, true>(st, sb, sa, qreg, (const u32x4*)k_stage(j + 2), v_stage(j + 1),
-                                                 (j + 2) * BC, q, Nk, sl2, col, hi, tr_row, tr_dd);
+        FA_TOP(j);
+        wave_step<D, CAUSAL, false, true>(st, sa, sb, qreg, FA_KS(j + 1), FA_V_STAGE(j), (j + 1) * BC, q, Nk,
+                                                 sl2, col, hi, tr_row, tr_dd);
+        FA_TOP(j + 1);
+        wave_step<D, CAUSAL, false, true>(st, sb, sa, qreg, FA_KS(j + 2), FA_V_STAGE(j + 1), (j + 2) * BC, q,
+                                                 Nk, sl2, col, hi, tr_row, tr_dd);
     }
     // The remaining steps (at most a few): masks on, per-wave skips.
     for (; j < n_kt; ++j) {
-        top(j);
+        FA_TOP(j);
         if (j < n_kt_wave) {
             if (j + 1 < n_kt_wave)
-                wave_step<D, CAUSAL, true, true, true>(st, sa, sb, qreg, (const u32x4*)k_stage(j + 1), v_stage(j),
-                                                       (j + 1) * BC, q, Nk, sl2, col, hi, tr_row, tr_dd);
+                wave_step<D, CAUSAL, true, true>(st, sa, sb, qreg, FA_KS(j + 1), FA_V_STAGE(j), (j + 1) * BC,
+                                                       q, Nk, sl2, col, hi, tr_row, tr_dd);
             else
-                wave_step<D, CAUSAL, true, true, false>(st, sa, sb, qreg, nullptr, v_stage(j), 0, q, Nk, sl2, col,
+                wave_step<D, CAUSAL, true, false>(st, sa, sb, qreg, nullptr, FA_V_STAGE(j), 0, q, Nk, sl2, col,
                                                         hi, tr_row, tr_dd);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
         }
     }
+
+#undef FA_K_STAGE
+#undef FA_V_STAGE
+#undef FA_ISSUE_K
+#undef FA_ISSUE_V
+#undef FA_TOP
+#undef FA_KS
 
     // ---- epilogue
     const float l_tot = pair_sum(st.l0 + st.l1);
@@ -549,7 +564,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
                 }
             }
         if (p.lse && hi == 0)
-            p.lse[(long long)bh * Nq + q] = (st.m + __log2f(l_tot)) * kLn2;
+            p.lse[(long long)bh * Nq + q] = (st.m + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
 }
 
@@ -567,14 +582,14 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(FwdParams p) {
     __shared__ float ks[BC * LD];
     __shared__ float vs[BC * LD];
 
-    const int tid = threadIdx.x;
+    const int tid = __builtin_amdgcn_workitem_id_x();
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int col = lane & 31;
     const int hi = lane >> 5;
 
     int bh, qt;
-    tile_of_block(blockIdx.x, p.n_qtiles, p.BH, CAUSAL, bh, qt);
+    tile_of_block(__builtin_amdgcn_workgroup_id_x(), p.n_qtiles, p.BH, CAUSAL, bh, qt);
     const int b = bh / p.H;
     const int h = bh - b * p.H;
     const int q_wg0 = qt * BR;
@@ -642,7 +657,7 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(FwdParams p) {
             sacc[r] = ok ? sacc[r] : -INFINITY;
             mx = fmaxf(mx, sacc[r]);
         }
-        mx = fmaxf(mx, xor32(mx));
+        mx = pair_max(mx);
         const float mt2 = (mx == -INFINITY) ? -INFINITY : mx * sl2;
         const bool move = mt2 > m_run + kLazyRescale;
         const float m_new = move ? mt2 : m_run;
@@ -673,7 +688,7 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(FwdParams p) {
             }
     }
 
-    const float l_tot = l_run + xor32(l_run);
+    const float l_tot = pair_sum(l_run);
     if (q < Nq) {
         const float inv = 1.0f / l_tot;
         float* obase = (float*)p.o + (long long)b * p.q_sb + (long long)h * p.q_sh + (long long)q * p.q_sn;
@@ -686,7 +701,7 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(FwdParams p) {
                                                      oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
             }
         if (p.lse && hi == 0)
-            p.lse[(long long)bh * Nq + q] = (m_run + __log2f(l_tot)) * kLn2;
+            p.lse[(long long)bh * Nq + q] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
 }
 
@@ -754,8 +769,9 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     const long long grid = n_qtiles * B * H;
     if ((long long)B * H > INT32_MAX || grid > INT32_MAX) return FA_ERR_UNSUPPORTED;
     // the bf16 kernel addresses a 64-row key tile with 32-bit byte offsets
+    // (and row offsets with 24-bit multiplies)
     const long long kv_row_bytes = (layout == FA_BSND ? (long long)H * d : (long long)d) * 2;
-    if (in_dtype == FA_BF16 && 64 * kv_row_bytes > INT32_MAX) return FA_ERR_UNSUPPORTED;
+    if (in_dtype == FA_BF16 && 64 * kv_row_bytes >= (1LL << 30)) return FA_ERR_UNSUPPORTED;
 
     if (scale < 0.f) scale = 1.0f / sqrtf((float)d);
 
@@ -772,7 +788,10 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     p.H = H; p.Nq = Nq; p.Nk = Nk;
     p.n_qtiles = (int)n_qtiles;
     p.BH = B * H;
-    p.scale_log2 = scale * kLog2e;
+    // scale 0 (uniform weights) runs as a tiny positive scale: every scaled
+    // score is then below 2^-24 in magnitude and every probability rounds to
+    // exactly 1, as with scale 0, while masked (-inf) scores still give 0.
+    p.scale_log2 = scale > 0.f ? scale * kLog2e : 1e-30f;
 
     hipStream_t s = (hipStream_t)stream;
     const bool c = causal != 0;
