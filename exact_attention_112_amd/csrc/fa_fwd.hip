@@ -333,10 +333,29 @@ __device__ __forceinline__ void wave_step(RowState<D>& st, f32x16 (&s_cur)[2], f
     }
 }
 
+// The same step without the overlap, for the few masked tiles at the end:
+// P_j and O += P_j V_j from the scores in s, then (HAS_NXT) the scores of
+// tile j+1, masked, into the same registers, and the max update.  Half the
+// score registers of wave_step.
+template <int D, bool CAUSAL, bool HAS_NXT>
+__device__ __forceinline__ void wave_step_serial(RowState<D>& st, f32x16 (&s)[2], const bf16x8 (&qreg)[D / 16],
+                                                 const u32x4* ks_nxt, const lds_char* vs_cur, int key0_nxt, int q,
+                                                 int Nk, float sl2, int col, int hi, int tr_row, int tr_dd) {
+    unsigned pk[2][8];
+    tile_exp(s, st.m, sl2, pk, st.l0, st.l1);
+    pv_tile<D>(st.oacc, pk, vs_cur, tr_row, tr_dd);
+    if constexpr (HAS_NXT) {
+        qk_tile<D>(s, qreg, ks_nxt, col, hi);
+        mask_tile<CAUSAL>(s, key0_nxt, q, Nk, hi);
+        update_max(st, tile_max_scaled(s, sl2));
+    }
+}
+
 // One 16-byte-per-lane buffer load into LDS: lane i of the wave writes the
-// 16 bytes at rsrc + voff to lds_dst + 16*i.
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, lds_char* lds_dst, unsigned voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_dst, 16, voff, 0, 0, 0);
+// 16 bytes at rsrc + soff + voff (soff wave-uniform) to lds_dst + 16*i.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, lds_char* lds_dst, unsigned voff,
+                                           unsigned soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_dst, 16, voff, (int)soff, 0, 0);
 }
 
 // A wave-uniform value moved to scalar registers (the compiler cannot always
@@ -347,24 +366,32 @@ __device__ __forceinline__ unsigned long long to_sgpr(unsigned long long a) {
     return ((unsigned long long)hi << 32) | lo;
 }
 
-// Issue the loads of one K or V tile into an LDS stage.  tile: address of the
-// tile's first row (wave-uniform); off: this lane's byte offsets inside a full
-// tile; nvalid: rows of the tile inside the sequence (rows past it re-read
-// the last valid row).
-template <int LPW, int DCH, int BC>
-__device__ __forceinline__ void issue_tile(unsigned long long tile, unsigned rb, const unsigned (&off)[LPW],
-                                           lds_char* dst, int nvalid, int wave, int lane) {
+// Issue the loads of one K or V tile into an LDS stage.  Load j of wave w
+// fills tile rows j*RPL + w*RPW .. +RPW-1 (RPW = 64/DCH rows per wave load,
+// RPL = NW*RPW rows per round of loads), all DCH chunks of each.
+//   tile: address of the tile's first row (wave-uniform)
+//   off: this lane's byte offset inside the tile for load 0; load j adds the
+//        uniform j*RPL*rb (the swizzles repeat every 16 rows and RPL is a
+//        multiple of 16 whenever LPW > 1, so the chunk part is the same)
+//   dst: this wave's LDS chunks of load 0; load j adds j*RPL rows
+//   nvalid: rows of the tile inside the sequence (rows past it re-read the
+//        last valid row)
+template <int LPW, int DCH, int BC, int NW>
+__device__ __forceinline__ void issue_tile(unsigned long long tile, unsigned rb, unsigned off, lds_char* dst,
+                                           int nvalid, int wave, int lane) {
+    constexpr int RPW = 64 / DCH, RPL = NW * RPW;
+    static_assert(LPW == 1 || RPL % 16 == 0, "load rounds must keep the swizzle phase");
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)to_sgpr(tile), (short)0, (int)(BC * rb), 0x00020000);
     if (nvalid >= BC) {
 #pragma unroll
-        for (int j = 0; j < LPW; ++j) load_lds16(rsrc, dst + j * 1024, off[j]);
+        for (int j = 0; j < LPW; ++j) load_lds16(rsrc, dst + j * RPL * DCH * 16, off, j * RPL * rb);
     } else {
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
-            const int row = ((wave * LPW + j) * 64 + lane) / DCH;
-            const unsigned o = off[j] - (unsigned)(row - min(row, nvalid - 1)) * rb;
-            load_lds16(rsrc, dst + j * 1024, o);
+            const int row = j * RPL + wave * RPW + lane / DCH;
+            const unsigned o = off - (unsigned)(row - min(row, nvalid - 1)) * rb;
+            load_lds16(rsrc, dst + j * RPL * DCH * 16, o, j * RPL * rb);
         }
     }
 }
@@ -438,32 +465,30 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     }
 
     // ---- direct HBM -> LDS staging (buffer_load ... lds, 16 bytes a lane).
-    // Each wave instruction writes 64 consecutive 16-byte LDS chunks; lane i
-    // of load j fills physical chunk pc = (wave*LPW + j)*64 + i, i.e. row
-    // pc/DCH, swizzled chunk pc%DCH, so it fetches the logical chunk
-    // (pc%DCH) ^ swz(row) (the swizzles are XORs, their own inverse).  The
-    // buffer descriptor is rebased on each tile (scalar), the lane offsets
-    // are fixed.  A tile that runs past Nk reads row Nk-1 in place of the
-    // missing rows: their scores are masked, and the V rows stay finite.
+    // Each wave instruction writes 64 consecutive 16-byte LDS chunks: RPW
+    // whole rows of the tile.  Lane i fills physical chunk i % DCH of its row,
+    // so it fetches the logical chunk (i % DCH) ^ swz(row) (the swizzles are
+    // XORs, their own inverse).  The buffer descriptor is rebased on each
+    // tile (scalar), the lane offset is fixed.  A tile that runs past Nk
+    // reads row Nk-1 in place of the missing rows: their scores are masked,
+    // and the V rows stay finite.
     const unsigned rb = (unsigned)row_bytes;
-    unsigned ld_koff[LPW], ld_voff[LPW];   // byte offsets inside a tile
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-        const int pc = (wave * LPW + j) * 64 + lane;
-        const int row = pc / DCH, ch = pc % DCH;
-        ld_koff[j] = row * rb + k_swz<D>(row, ch) * 16;
-        ld_voff[j] = row * rb + v_swz<D>(row, ch) * 16;
+    unsigned ld_koff, ld_voff;   // byte offsets inside a tile (load round 0)
+    {
+        const int row = wave * (64 / DCH) + lane / DCH, ch = lane % DCH;
+        ld_koff = row * rb + k_swz<D>(row, ch) * 16;
+        ld_voff = row * rb + v_swz<D>(row, ch) * 16;
     }
     lds_char* const lds = (lds_char*)smem;
     const unsigned long long kaddr = to_sgpr((unsigned long long)kbase);
     const unsigned long long vaddr = to_sgpr((unsigned long long)vbase);
     const unsigned long long tile_bytes = (unsigned long long)BC * (unsigned long long)row_bytes;
-    lds_char* const ldst = lds + wave * LPW * 1024;   // this wave's part of a stage
+    lds_char* const ldst = lds + wave * 1024;   // this wave's rows of load round 0 in a stage
 #define FA_K_STAGE(t) (lds + ((t) & 1) * TB)
 #define FA_V_STAGE(t) (lds + (2 + ((t) & 1)) * TB)
-#define FA_ISSUE_K(t) issue_tile<LPW, DCH, BC>(kaddr + (unsigned long long)(t) * tile_bytes, rb, ld_koff, \
+#define FA_ISSUE_K(t) issue_tile<LPW, DCH, BC, NW>(kaddr + (unsigned long long)(t) * tile_bytes, rb, ld_koff, \
                                               ldst + ((t) & 1) * TB, Nk - (t) * BC, wave, lane)
-#define FA_ISSUE_V(t) issue_tile<LPW, DCH, BC>(vaddr + (unsigned long long)(t) * tile_bytes, rb, ld_voff, \
+#define FA_ISSUE_V(t) issue_tile<LPW, DCH, BC, NW>(vaddr + (unsigned long long)(t) * tile_bytes, rb, ld_voff, \
                                               ldst + (2 + ((t) & 1)) * TB, Nk - (t) * BC, wave, lane)
 
     RowState<D> st;
@@ -521,18 +546,17 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         wave_step<D, CAUSAL, false, true>(st, sb, sa, qreg, FA_KS(j + 2), FA_V_STAGE(j + 1), (j + 2) * BC, q,
                                                  Nk, sl2, col, hi, tr_row, tr_dd);
     }
-    // The remaining steps (at most a few): masks on, per-wave skips.
+    // The remaining steps (at most a few): masks on, per-wave skips, no
+    // overlap (one score buffer).
     for (; j < n_kt; ++j) {
         FA_TOP(j);
         if (j < n_kt_wave) {
             if (j + 1 < n_kt_wave)
-                wave_step<D, CAUSAL, true, true>(st, sa, sb, qreg, FA_KS(j + 1), FA_V_STAGE(j), (j + 1) * BC,
-                                                       q, Nk, sl2, col, hi, tr_row, tr_dd);
+                wave_step_serial<D, CAUSAL, true>(st, sa, qreg, FA_KS(j + 1), FA_V_STAGE(j), (j + 1) * BC, q, Nk,
+                                                  sl2, col, hi, tr_row, tr_dd);
             else
-                wave_step<D, CAUSAL, true, false>(st, sa, sb, qreg, nullptr, FA_V_STAGE(j), 0, q, Nk, sl2, col,
-                                                        hi, tr_row, tr_dd);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
+                wave_step_serial<D, CAUSAL, false>(st, sa, qreg, nullptr, FA_V_STAGE(j), 0, q, Nk, sl2, col, hi,
+                                                   tr_row, tr_dd);
         }
     }
 
@@ -545,6 +569,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 
     // ---- epilogue
     const float l_tot = pair_sum(st.l0 + st.l1);
+    // the lane's half, recomputed (mbcnt) rather than kept live through the loops
+    const int hi_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5;
     if (q < Nq) {
         const float inv = 1.0f / l_tot;
         char* obase = (char*)p.o;
@@ -553,7 +579,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int dd = db * 32 + g * 8 + hi * 4;
+                const int dd = db * 32 + g * 8 + hi_e * 4;
                 const float o0 = st.oacc[db][4 * g + 0] * inv, o1 = st.oacc[db][4 * g + 1] * inv;
                 const float o2 = st.oacc[db][4 * g + 2] * inv, o3 = st.oacc[db][4 * g + 3] * inv;
                 if constexpr (OUT_BF16) {
@@ -563,7 +589,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
                     *(float4*)(obase + (orow + dd) * 4) = make_float4(o0, o1, o2, o3);
                 }
             }
-        if (p.lse && hi == 0)
+        if (p.lse && hi_e == 0)
             p.lse[(long long)bh * Nq + q] = (st.m + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
 }
