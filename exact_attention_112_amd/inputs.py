@@ -6,7 +6,7 @@ the attention arithmetic.
 
 Recipe (one ``numpy.random.Generator(PCG64(seed))`` per tensor, seed =
 1000 * config_id + t with t = 0 for Q, 1 for K, 2 for V, 3 for the choice of
-peaked key rows):
+peaked key rows, 4 for the upstream gradient dO of the backward pass):
 
 * values are float32 ``standard_normal`` draws in the *storage order* of the
   workload's layout (BHND = [B,H,N,d], BSND = [B,N,H,d]), times the tensor's
@@ -180,6 +180,18 @@ def make_inputs(w: Workload, seed_base: int | None = None) -> Inputs:
     if w.dtype != "f32":
         raise ValueError(f"unknown dtype {w.dtype!r}")
     return Inputs(w, q, k, v, None, None, None, pos)
+
+
+def make_grad(w: Workload, seed_base: int | None = None):
+    """The upstream gradient dO (shape and layout of Q) for the backward pass:
+    N(0, 1) draws from seed 1000*cid+4 (or seed_base+4), rounded to bf16 for
+    bf16 workloads.  Returns (float32 values, bf16 bits or None)."""
+    base = 1000 * w.cid if seed_base is None else seed_base
+    g = _draw(base + 4, w.q_shape(), 1.0)
+    if w.dtype == "bf16":
+        gb = f32_to_bf16_bits(g)
+        return bf16_bits_to_f32(gb), gb
+    return g, None
 
 
 def sample_rows(w: Workload, n: int, seed: int = 7, peaked: np.ndarray | None = None) -> np.ndarray:

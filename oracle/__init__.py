@@ -1,11 +1,12 @@
-"""CPU oracle for the attention forward pass -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the attention forward and backward passes -- TEST
+INFRASTRUCTURE ONLY.
 
 Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product library never calls it, and
 it shares no code with the GPU path (the only common module is the seeded
 input generator, which holds none of the method's arithmetic).
 
-Two implementations live here:
+Three implementations live here:
 
 * ``attn_fwd`` -- the plain definition, a two-pass fp64 softmax attention in C
   (``oracle.c``): scores, row max, exp-sum, weighted sum of values, one row at
@@ -13,6 +14,11 @@ Two implementations live here:
   (S = QK^T/sqrt(d), P = softmax(S), O = PV), [nanhubrain] "online softmax
   mathematics" (max-subtracted softmax) and [ascendai] section 6.1 (causal:
   strict upper triangle masked, key j visible to query i iff j <= i).
+* ``attn_bwd`` -- the gradients dQ, dK, dV of the same attention for an
+  upstream gradient dO, by their plain definition in fp64 C (``oracle.c``):
+  P, dP = dO V^T, D_i = rowsum(P * dP) over the whole row, dS = P * (dP - D),
+  dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO ([nanhubrain] "backward
+  recomputation", with the row term taken over the whole row).
 * ``online.attn_fwd_online`` -- the pages' own algorithm, the tiled forward
   with the online-softmax recurrence ([nanhubrain] "tiling skeleton",
   [ascendai] section 2.2), in numpy fp64, over caller-chosen block splits.
@@ -64,6 +70,10 @@ class OracleLib:
         g.restype = _c_int
         g.argtypes = [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_int, _c_int, _c_int,
                       _c_dbl, _c_int, _c_ptr]
+        h = self._lib.oracle_attn_bwd
+        h.restype = _c_int
+        h.argtypes = ([_c_ptr] * 4 + [_c_i64] * 6 + [_c_int] * 5 + [_c_dbl, _c_int]
+                      + [_c_ptr, _c_int, _c_ptr, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_int])
         self._lib.oracle_max_threads.restype = _c_int
 
     def max_threads(self) -> int:
@@ -113,6 +123,55 @@ class OracleLib:
             raise RuntimeError(f"oracle_attn_fwd failed with code {rc}")
         return o, lse
 
+    def attn_bwd(self, q, k, v, do, *, scale: float, causal: bool = False,
+                 layout: str = "BHND", qrows=None, krows=None, want_dq: bool = True,
+                 want_dkv: bool = True, n_threads: int = 0):
+        """(dQ [B,H,RQ,d], dK [B,H,RK,d], dV [B,H,RK,d]) in float64 (None for
+        the parts not asked for).
+
+        q, k, v, do: float32 arrays in the layout's storage shape (do has q's
+        shape).  ``qrows`` / ``krows``: optional query / key indices (the same
+        for every (b, h)); default all rows.
+        """
+        q = np.ascontiguousarray(q, dtype=np.float32)
+        k = np.ascontiguousarray(k, dtype=np.float32)
+        v = np.ascontiguousarray(v, dtype=np.float32)
+        do = np.ascontiguousarray(do, dtype=np.float32)
+        if q.shape != do.shape or k.shape != v.shape:
+            raise ValueError("do must have q's shape and v k's shape")
+        if layout == "BHND":
+            B, H, Nq, d = q.shape
+            Nk = k.shape[2]
+            qs = (H * Nq * d, Nq * d, d)
+            ks = (H * Nk * d, Nk * d, d)
+        elif layout == "BSND":
+            B, Nq, H, d = q.shape
+            Nk = k.shape[1]
+            qs = (Nq * H * d, d, H * d)
+            ks = (Nk * H * d, d, H * d)
+        else:
+            raise ValueError(f"unknown layout {layout!r}")
+
+        def idx(rows, n):
+            if rows is None:
+                return None, None, n
+            a = np.ascontiguousarray(rows, dtype=np.int32)
+            return a, a.ctypes.data, int(a.size)
+
+        qa, qp, RQ = idx(qrows, Nq)
+        ka, kp, RK = idx(krows, Nk)
+        dq = np.empty((B, H, RQ, d), dtype=np.float64) if want_dq else None
+        dk = np.empty((B, H, RK, d), dtype=np.float64) if want_dkv else None
+        dv = np.empty((B, H, RK, d), dtype=np.float64) if want_dkv else None
+        ptr = lambda a: None if a is None else a.ctypes.data
+        rc = self._lib.oracle_attn_bwd(
+            q.ctypes.data, k.ctypes.data, v.ctypes.data, do.ctypes.data,
+            *qs, *ks, B, H, Nq, Nk, d, float(scale), int(bool(causal)),
+            qp, RQ, kp, RK, ptr(dq), ptr(dk), ptr(dv), int(n_threads))
+        if rc != 0:
+            raise RuntimeError(f"oracle_attn_bwd failed with code {rc}")
+        return dq, dk, dv
+
     def attn_probs(self, q, k, *, scale: float, causal: bool = False):
         """P [Nq, Nk] (float64) of one head; q [Nq,d], k [Nk,d] float32."""
         q = np.ascontiguousarray(q, dtype=np.float32)
@@ -147,3 +206,7 @@ def attn_fwd(q, k, v, **kw):
 
 def attn_probs(q, k, **kw):
     return lib().attn_probs(q, k, **kw)
+
+
+def attn_bwd(q, k, v, do, **kw):
+    return lib().attn_bwd(q, k, v, do, **kw)

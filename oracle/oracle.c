@@ -1,5 +1,6 @@
 /*
- * oracle.c -- plain fp64 CPU reference for the attention forward pass.
+ * oracle.c -- plain fp64 CPU reference for the attention forward pass and its
+ * gradients (the backward pass, near the end of the file).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes or
  * calls this file; only the test suite, the smoke check and the benchmark's
@@ -172,3 +173,167 @@ int oracle_attn_probs(const float* q, const float* k,
 
 /* Threads an OpenMP parallel region would use by default. */
 int oracle_max_threads(void) { return omp_get_max_threads(); }
+
+/* ------------------------------------------------------------------------
+ * Backward pass (gradients of a loss L through O), in double.
+ *
+ * For one (b, h), with P the forward's probabilities and dO = dL/dO:
+ *   dV_j  = sum_i P_ij dO_i
+ *   dP_ij = dO_i . v_j
+ *   D_i   = sum_j P_ij dP_ij          (the whole visible row)
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ_i  = scale * sum_j dS_ij k_j
+ *   dK_j  = scale * sum_i dS_ij q_i
+ * over visible pairs only (masked pairs have P = 0 and carry no gradient).
+ *
+ * [nanhubrain] section "backward recomputation" rebuilds P from the row
+ * statistics and accumulates dV += P^T dO, dP = dO V^T,
+ * dS = P * (dP - rowsum(P * dP)), dQ += dS K, dK += dS^T Q block by block.
+ * Its row term is summed over one key block only; the derivative of the
+ * softmax needs it over the whole row (D_i above, which also equals
+ * dO_i . O_i), and that is what is computed here.  The score scale
+ * (S = scale * Q K^T) enters dQ and dK by the chain rule; the listing's
+ * 1/sqrt(d) is that scale.
+ * ---------------------------------------------------------------------- */
+
+/* Row pass for query i of one (b, h): P_ij into p[], dP_ij into g[] (visible
+ * j only), the row's log-sum-exp and D_i.  Returns the visible count. */
+static int grad_row(const float* qi, const float* gi, const float* kbh, const float* vbh,
+                    int64_t k_sn, int Nk, int d, double scale, int causal, int i,
+                    double* p, double* g, double* lse_i, double* D_i)
+{
+    int vis = Nk;
+    if (causal && i + 1 < vis) vis = i + 1;
+    double top = -INFINITY;
+    for (int j = 0; j < vis; ++j) {
+        const float* kj = kbh + (int64_t)j * k_sn;
+        const float* vj = vbh + (int64_t)j * k_sn;
+        double a = 0.0, b = 0.0;
+        for (int c = 0; c < d; ++c) {
+            a += (double)qi[c] * (double)kj[c];
+            b += (double)gi[c] * (double)vj[c];
+        }
+        p[j] = scale * a;
+        g[j] = b;
+        if (p[j] > top) top = p[j];
+    }
+    double z = 0.0;
+    for (int j = 0; j < vis; ++j) z += exp(p[j] - top);
+    const double lse = top + log(z);
+    double D = 0.0;
+    for (int j = 0; j < vis; ++j) {
+        p[j] = exp(p[j] - lse);
+        D += p[j] * g[j];
+    }
+    *lse_i = lse;
+    *D_i = D;
+    return vis;
+}
+
+/*
+ * oracle_attn_bwd: dQ [B,H,RQ,d], dK and dV [B,H,RK,d] in double, where the
+ * RQ query rows are qrows[0..n_qrows) (all Nq when qrows == NULL) and the RK
+ * key rows krows[0..n_krows) (all Nk when krows == NULL).  dq == NULL skips
+ * dQ; dk == NULL or dv == NULL skips dK and dV.  dO uses Q's strides, V uses
+ * K's.  Returns 0, -1 on bad arguments, -2 on allocation failure.
+ */
+int oracle_attn_bwd(const float* q, const float* k, const float* v, const float* dout,
+                    int64_t q_sb, int64_t q_sh, int64_t q_sn,
+                    int64_t k_sb, int64_t k_sh, int64_t k_sn,
+                    int B, int H, int Nq, int Nk, int d,
+                    double scale, int causal,
+                    const int32_t* qrows, int n_qrows, const int32_t* krows, int n_krows,
+                    double* dq, double* dk, double* dv, int n_threads)
+{
+    if (!q || !k || !v || !dout) return -1;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return -1;
+    const int RQ = qrows ? n_qrows : Nq, RK = krows ? n_krows : Nk;
+    if (RQ < 0 || RK < 0) return -1;
+    for (int r = 0; qrows && r < RQ; ++r)
+        if (qrows[r] < 0 || qrows[r] >= Nq) return -1;
+    for (int r = 0; krows && r < RK; ++r)
+        if (krows[r] < 0 || krows[r] >= Nk) return -1;
+    const int want_kv = dk && dv;
+    if (n_threads <= 0) n_threads = omp_get_max_threads();
+
+    double* stat = (double*)malloc(sizeof(double) * 2 * (size_t)Nq);
+    if (!stat) return -2;
+    double* lse = stat;
+    double* Dr = stat + Nq;
+    int status = 0;
+
+    for (int bh = 0; bh < B * H && status == 0; ++bh) {
+        const int b = bh / H, h = bh % H;
+        const float* qbh = q + b * q_sb + h * q_sh;
+        const float* gbh = dout + b * q_sb + h * q_sh;
+        const float* kbh = k + b * k_sb + h * k_sh;
+        const float* vbh = v + b * k_sb + h * k_sh;
+
+        /* pass 1: row statistics (lse_i, D_i) of every query; pass 2: dQ of
+         * the requested rows, from the same row pass */
+#pragma omp parallel num_threads(n_threads)
+        {
+            double* p = (double*)malloc(sizeof(double) * 2 * (size_t)Nk);
+            if (!p) {
+#pragma omp atomic write
+                status = -2;
+            }
+#pragma omp for schedule(dynamic, 8)
+            for (int i = 0; i < Nq; ++i) {
+                if (!p) continue;
+                grad_row(qbh + (int64_t)i * q_sn, gbh + (int64_t)i * q_sn, kbh, vbh, k_sn, Nk, d,
+                         scale, causal, i, p, p + Nk, &lse[i], &Dr[i]);
+            }
+            if (dq) {
+#pragma omp for schedule(dynamic, 4)
+                for (int r = 0; r < RQ; ++r) {
+                    if (!p) continue;
+                    const int i = qrows ? qrows[r] : r;
+                    double unused_lse, Di;
+                    const int vis = grad_row(qbh + (int64_t)i * q_sn, gbh + (int64_t)i * q_sn, kbh, vbh,
+                                             k_sn, Nk, d, scale, causal, i, p, p + Nk, &unused_lse, &Di);
+                    double* out = dq + ((int64_t)bh * RQ + r) * d;
+                    for (int c = 0; c < d; ++c) out[c] = 0.0;
+                    for (int j = 0; j < vis; ++j) {
+                        const double ds = p[j] * (p[Nk + j] - Di);
+                        const float* kj = kbh + (int64_t)j * k_sn;
+                        for (int c = 0; c < d; ++c) out[c] += ds * (double)kj[c];
+                    }
+                    for (int c = 0; c < d; ++c) out[c] *= scale;
+                }
+            }
+            free(p);
+        }
+        if (status != 0 || !want_kv) continue;
+
+        /* pass 3: dK and dV of the requested key rows, one column at a time,
+         * from the row statistics of pass 1 */
+#pragma omp parallel for num_threads(n_threads) schedule(dynamic, 4)
+        for (int r = 0; r < RK; ++r) {
+            const int j = krows ? krows[r] : r;
+            const float* kj = kbh + (int64_t)j * k_sn;
+            const float* vj = vbh + (int64_t)j * k_sn;
+            double* gk = dk + ((int64_t)bh * RK + r) * d;
+            double* gv = dv + ((int64_t)bh * RK + r) * d;
+            for (int c = 0; c < d; ++c) gk[c] = gv[c] = 0.0;
+            for (int i = causal ? j : 0; i < Nq; ++i) {
+                const float* qi = qbh + (int64_t)i * q_sn;
+                const float* gi = gbh + (int64_t)i * q_sn;
+                double a = 0.0, e = 0.0;
+                for (int c = 0; c < d; ++c) {
+                    a += (double)qi[c] * (double)kj[c];
+                    e += (double)gi[c] * (double)vj[c];
+                }
+                const double pij = exp(scale * a - lse[i]);
+                const double ds = pij * (e - Dr[i]);
+                for (int c = 0; c < d; ++c) {
+                    gv[c] += pij * (double)gi[c];
+                    gk[c] += ds * (double)qi[c];
+                }
+            }
+            for (int c = 0; c < d; ++c) gk[c] *= scale;
+        }
+    }
+    free(stat);
+    return status;
+}
