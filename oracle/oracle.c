@@ -264,10 +264,12 @@ int oracle_attn_bwd(const float* q, const float* k, const float* v, const float*
 
     for (int bh = 0; bh < B * H && status == 0; ++bh) {
         const int b = bh / H, h = bh % H;
-        const float* qbh = q + b * q_sb + h * q_sh;
-        const float* gbh = dout + b * q_sb + h * q_sh;
-        const float* kbh = k + b * k_sb + h * k_sh;
-        const float* vbh = v + b * k_sb + h * k_sh;
+        const int64_t qoff = (int64_t)b * q_sb + (int64_t)h * q_sh;
+        const int64_t koff = (int64_t)b * k_sb + (int64_t)h * k_sh;
+        const float* qbh = q + qoff;
+        const float* gbh = dout + qoff;
+        const float* kbh = k + koff;
+        const float* vbh = v + koff;
 
         /* pass 1: row statistics (lse_i, D_i) of every query; pass 2: dQ of
          * the requested rows, from the same row pass */
