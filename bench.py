@@ -41,13 +41,17 @@ def algorithmic_bytes(w, out_bytes: int) -> float:
     return float(per_head) * w.B * w.H
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_112_amd", "csrc", "fa_fwd.hip")
+# the forward kernel's sources (its file and the shared device header)
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_112_amd", "csrc", n) for n in ("fa_fwd.hip", "fa_common.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(workload: str):

@@ -1,4 +1,5 @@
-"""libfa355: attention forward pass on AMD Instinct MI355X (gfx950).
+"""libfa355: attention forward and backward passes on AMD Instinct MI355X
+(gfx950).
 
 Python binding of the C ABI in ``include/fa355.h``: argument marshalling only.
 Every step of the computation runs in the HIP kernels of ``libfa355.so``;
@@ -12,6 +13,12 @@ computes O = softmax(scale * Q K^T [causal]) V per (batch, head) and the
 per-row natural-log log-sum-exp (pages: [nanhubrain] = nanhubrain.csdn.net
 "exact source of the quadratic memory", "tiling skeleton", "online softmax
 mathematics"; [ascendai] = ascendai.csdn.net sections 3.1 and 6.1).
+
+    dQ, dK, dV = bwd(q, k, v, o, do, lse, causal=False, scale=None, layout="BHND")
+
+computes the gradients for an upstream gradient dO, rebuilding P from the LSE
+([nanhubrain] "backward recomputation"; the row term dO_i . O_i is taken over
+the whole row).  Outputs are float32 in the layouts of q and k.
 """
 from __future__ import annotations
 
@@ -27,7 +34,7 @@ FA_BF16, FA_F32 = 0, 1
 LAYOUTS = {"BHND": FA_BHND, "BSND": FA_BSND}
 
 # the symbols include/fa355.h declares
-EXPORTS = ("fa_fwd", "fa_status_str", "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_status_str", "fa_abi_version")
 ABI_VERSION = 1
 
 _lib = None
@@ -61,6 +68,9 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     lib.fa_fwd.restype = ctypes.c_int
     lib.fa_fwd.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_float]
+                           + [ctypes.c_int] * 4 + [ctypes.c_void_p])
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float]
                            + [ctypes.c_int] * 4 + [ctypes.c_void_p])
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [ctypes.c_int]
@@ -144,3 +154,74 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, layout: st
     if st != FA_OK:
         raise FaError(st, "HIP launch failed")
     return out, lse
+
+
+def fa_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int, delta: int,
+           B: int, H: int, Nq: int, Nk: int, d: int, scale: float, causal: int, layout: int,
+           in_dtype: int, o_dtype: int, stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the fa_status."""
+    return int(load().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d, float(scale),
+                             int(causal), int(layout), int(in_dtype), int(o_dtype), stream or None))
+
+
+def bwd(q, k, v, o, do, lse, *, causal: bool = False, scale: float | None = None, layout: str = "BHND",
+        dq=None, dk=None, dv=None, delta=None):
+    """Attention backward on torch CUDA tensors (ROCm).
+
+    q, k, v, do: bf16, contiguous, in ``layout`` (do has q's shape); o: the
+    forward output (float32 or bfloat16, q's shape); lse: float32 [B,H,Nq]
+    from the forward pass.  Returns (dQ, dK, dV), float32 in the layouts of
+    q and k.  ``delta`` (float32 [B,H,Nq]) is the workspace for D_i; it is
+    allocated here when not given.  Enqueued on the current stream.
+    """
+    import torch
+
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {list(LAYOUTS)}")
+    ts = (q, k, v, o, do, lse)
+    if any(not t.is_cuda for t in ts) or len({t.device for t in ts}) != 1:
+        raise ValueError("all tensors must be on one GPU")
+    if not all(t.is_contiguous() for t in ts):
+        raise ValueError("all tensors must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype == do.dtype == torch.bfloat16):
+        raise ValueError("q, k, v and do must be bfloat16")
+    if o.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("o must be float32 or bfloat16")
+    if q.dim() != 4 or k.shape != v.shape or k.dim() != 4 or do.shape != q.shape or o.shape != q.shape:
+        raise ValueError("q, o, do must share a 4-D shape; k and v another")
+    if layout == "BHND":
+        B, H, Nq, d = q.shape
+        Bk, Hk, Nk, dk_ = k.shape
+    else:
+        B, Nq, H, d = q.shape
+        Bk, Nk, Hk, dk_ = k.shape
+    if (Bk, Hk, dk_) != (B, H, d):
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree for layout {layout}")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B,H,Nq]")
+
+    def out(t, shape, name):
+        if t is None:
+            return torch.empty(shape, dtype=torch.float32, device=q.device)
+        if t.shape != tuple(shape) or t.dtype != torch.float32 or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)} on q's device")
+        return t
+
+    dq = out(dq, q.shape, "dq")
+    dk = out(dk, k.shape, "dk")
+    dv = out(dv, k.shape, "dv")
+    delta = out(delta, (B, H, Nq), "delta")
+    o_dt = FA_BF16 if o.dtype == torch.bfloat16 else FA_F32
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, Nq, Nk, d,
+                    -1.0 if scale is None else float(scale), int(bool(causal)), LAYOUTS[layout],
+                    FA_BF16, o_dt, stream)
+    if st == FA_ERR_INVALID_ARG:
+        raise FaInvalidArgument(st, "invalid argument")
+    if st == FA_ERR_UNSUPPORTED:
+        raise FaUnsupported(st, "unsupported configuration")
+    if st != FA_OK:
+        raise FaError(st, "HIP launch failed")
+    return dq, dk, dv

@@ -1,0 +1,573 @@
+// fa_bwd.hip -- attention backward pass for gfx950 (AMD Instinct MI355X).
+//
+// Gradients dQ, dK, dV of O = softmax(scale * Q K^T [causal]) V for an
+// upstream gradient dO.  Method ([nanhubrain] = nanhubrain.csdn.net,
+// FlashAttention in CANN ops-transformer, section "backward recomputation"):
+// the probabilities are not stored by the forward pass but rebuilt tile by
+// tile from its per-row statistics, here the log-sum-exp
+// (P_ij = exp(scale * q_i.k_j - LSE_i)), and the gradient chain is
+//   dV += P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ += dS K,  dK += dS^T Q
+// with the score scale entering dQ and dK.  The row term D_i must be summed
+// over the whole row, D_i = sum_j P_ij dP_ij, which equals dO_i . O_i; the
+// listing's sum over one key block is not the softmax derivative.  D is
+// computed once per row from O and dO.
+//
+// gfx950 design (three kernels on one stream; no atomics, so results are
+// deterministic):
+//   1. delta:  D = rowsum(dO * O) into a caller-provided float32 workspace.
+//   2. dK/dV:  key blocks outer (128 keys per workgroup, 32 per wave), query
+//      tiles of 32 inner.  The wave's K^T fragment stays in VGPRs, its dK^T
+//      and dV^T accumulators (fp32) too; the workgroup's V block sits in LDS
+//      for the whole loop.  Q and dO tiles go HBM -> LDS directly, two
+//      stages, and are read both as MFMA rows (ds_read_b128, for S = Q K^T
+//      and dP = dO V^T) and transposed (ds_read_b64_tr_b16, for
+//      dV^T += dO^T P and dK^T += Q^T dS).  A lane owns one key: S and dP
+//      come out with the key as the lane's column, so P and dS, packed to
+//      bf16, are directly the B operands of the two accumulations.
+//   3. dQ:     query tiles outer, like the forward kernel (32 queries per
+//      wave, key tiles of 64 inner, two LDS stages for K and V).  Q and dO
+//      fragments stay in VGPRs; S^T = K Q^T and dP^T = V dO^T give a lane
+//      one query, so LSE_i and D_i are per-lane scalars, and
+//      dQ^T += K^T dS^T reads K^T through transposing LDS reads.
+// All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS
+// are rounded to bf16 (RNE) as MFMA operands.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "fa355.h"
+#include "fa_common.h"
+
+namespace fa355 {
+
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    const float* lse;
+    float* dq;
+    float* dk;
+    float* dv;
+    float* delta;
+    long long q_sb, q_sh, q_sn;   // element strides of Q, O, dO and dQ (batch, head, row)
+    long long k_sb, k_sh, k_sn;   // element strides of K, V, dK and dV
+    int H, Nq, Nk;
+    int n_tiles;                  // row tiles of the kernel's outer loop
+    int BH;                       // B * H
+    float scale;                  // softmax scale (>= 0)
+    float scale_log2;             // scale * log2(e); a tiny positive value for scale 0
+};
+
+// Swizzle selector for the LDS tiles: 0 = k_swz (rows read only with
+// ds_read_b128), 2 = kv_swz (rows read both ways).
+template <int D, int SWZ>
+__device__ __forceinline__ int swz(int row, int ch) {
+    if constexpr (SWZ == 0) return k_swz<D>(row, ch);
+    else return kv_swz<D>(row, ch);
+}
+
+// acc[kb] = A_kb B for 32 rows of A per kb: A rows from an LDS tile (row
+// kb*32 + col, chunks 2kk + hi of 8 bf16), B fragments in registers
+// (bfrag[kk] = 8 values along the contraction for this lane's column).
+template <int D, int NKB, int SWZ>
+__device__ __forceinline__ void rows_times_frag(f32x16 (&acc)[NKB], const bf16x8 (&bfrag)[D / 16],
+                                                const u32x4* __restrict__ tile, int col, int hi) {
+    constexpr int DCH = D / 8, KK = D / 16;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const int row = kb * 32 + col;
+            const u32x4 a = tile[row * DCH + swz<D, SWZ>(row, 2 * kk + hi)];
+            const f32x16 c = kk == 0 ? f32x16{} : acc[kb];
+            acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), bfrag[kk], c, 0, 0, 0);
+        }
+    }
+}
+
+// acc[db] += T^T X for a tile T of 32*NKB rows in LDS (read transposed) and X
+// the packed bf16 operand of those rows in the 32x32 output layout of a
+// previous product (pk[kb][j] = rows (kb*32 + 2j, +1) of the lane's column,
+// in the permuted order the MFMA contraction accepts): slots 0..3 of 16-row
+// group u are rows 16u + hi*4 + 0..3, slots 4..7 rows 16u + 8 + hi*4 + 0..3.
+template <int D, int NKB>
+__device__ __forceinline__ void tr_times_packed(f32x16 (&acc)[D / 32], const unsigned (&pk)[NKB][8],
+                                                const lds_char* tile, int tr_row, int tr_dd) {
+    constexpr int DB = D / 32;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const bf16x8 pb = __builtin_bit_cast(
+                bf16x8, (u32x4){pk[kb][4 * u + 0], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]});
+            const int r0 = kb * 32 + 16 * u + tr_row;
+            const int r1 = r0 + 8;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int dd = db * 32 + tr_dd;
+                const int c = dd >> 3, w = (dd & 7) * 2;
+                const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4*)(tile + r0 * (D * 2) + kv_swz<D>(r0, c) * 16 + w));
+                const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4*)(tile + r1 * (D * 2) + kv_swz<D>(r1, c) * 16 + w));
+                const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc[db], 0, 0, 0);
+            }
+        }
+    }
+}
+
+// Row-major bf16 fragment from global memory: 8 values at column 16kk + 8hi
+// of row `row` for every kk (zero when the row is past the sequence).
+template <int D>
+__device__ __forceinline__ void load_frag(bf16x8 (&f)[D / 16], const __bf16* base, long long row_stride, int row,
+                                          int nrows, int hi) {
+    const bool ok = row < nrows;
+    const __bf16* r = base + (long long)(ok ? row : 0) * row_stride + hi * 8;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        const u32x4 x = ok ? *(const u32x4*)(r + kk * 16) : (u32x4){0u, 0u, 0u, 0u};
+        f[kk] = __builtin_bit_cast(bf16x8, x);
+    }
+}
+
+// Store a d x 32 accumulator (transposed: lane column = the row of the
+// output, registers = d) times `mul` as fp32 rows of the output.
+template <int D>
+__device__ __forceinline__ void store_rows_f32(float* out_row, const f32x16 (&acc)[D / 32], float mul, int hi) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int dd = db * 32 + g * 8 + hi * 4;
+            *(float4*)(out_row + dd) = make_float4(acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul,
+                                                   acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul);
+        }
+}
+
+// ---------------------------------------------------------------------------
+// 1. D_i = dO_i . O_i, one row per D/8 threads (8 elements each).
+template <int D, bool O_BF16>
+__global__ __launch_bounds__(256) void fa_bwd_delta_kernel(BwdParams p) {
+    constexpr int TPR = D / 8, RPB = 256 / TPR;
+    const int tid = __builtin_amdgcn_workitem_id_x();
+    const long long r = (long long)__builtin_amdgcn_workgroup_id_x() * RPB + tid / TPR;
+    const int part = tid % TPR;
+    const long long total = (long long)p.BH * p.Nq;
+    float acc = 0.f;
+    if (r < total) {
+        const long long bh = r / p.Nq, i = r - bh * p.Nq;
+        const long long b = bh / p.H, h = bh - b * p.H;
+        const long long off = b * p.q_sb + h * p.q_sh + i * p.q_sn + part * 8;
+        const bf16x8 g = __builtin_bit_cast(bf16x8, *(const u32x4*)((const __bf16*)p.dout + off));
+        if constexpr (O_BF16) {
+            const bf16x8 o = __builtin_bit_cast(bf16x8, *(const u32x4*)((const __bf16*)p.o + off));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)g[e], (float)o[e], acc);
+        } else {
+            const float4 o0 = *(const float4*)((const float*)p.o + off);
+            const float4 o1 = *(const float4*)((const float*)p.o + off + 4);
+            const float of[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)g[e], of[e], acc);
+        }
+    }
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, TPR);
+    if (r < total && part == 0) p.delta[r] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK and dV: key blocks outer.
+//
+// Register layout of one wave (32 keys; lane = (col, hi), col = lane % 32 is
+// the key, hi = lane / 32):
+//   S and dP of a 32-query tile: s[r] = query (r/4)*8 + hi*4 + r%4 of the
+//   tile against key col;
+//   dK^T, dV^T accumulators: acc[db][r] = d index db*32 + (r/4)*8 + hi*4 + r%4
+//   of key col.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dkdv_kernel(BwdParams p) {
+    constexpr int NW = 4, BK = NW * 32, BQ = 32, DCH = D / 8, KK = D / 16, DB = D / 32;
+    constexpr int QT_CH = BQ * DCH, QTB = QT_CH * 16;     // one Q (or dO) tile
+    constexpr int VB_CH = BK * DCH;                       // the V block
+    constexpr int LPWQ = QT_CH / 64 / NW, LPWV = VB_CH / 64 / NW;
+    static_assert(QT_CH % (64 * NW) == 0 && VB_CH % (64 * NW) == 0, "tiles must split evenly");
+
+    // V block, then Q stages 0, 1, then dO stages 0, 1
+    __shared__ u32x4 smem[VB_CH + 4 * QT_CH];
+    __shared__ __attribute__((aligned(16))) float stat[2][2][BQ];   // [stage][lse*log2e, D][query]
+
+    const int tid = __builtin_amdgcn_workitem_id_x();
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31;
+    const int hi = lane >> 5;
+
+    int bh, kt;
+    tile_of_block(__builtin_amdgcn_workgroup_id_x(), p.n_tiles, p.BH, CAUSAL, bh, kt);
+    if (CAUSAL) kt = p.n_tiles - 1 - kt;   // the longest key blocks (first keys) first
+    const int b = bh / p.H;
+    const int h = bh - b * p.H;
+    const int Nq = p.Nq, Nk = p.Nk;
+    const int k0 = kt * BK;               // first key of the workgroup
+    const int kw0 = k0 + wave * 32;       // first key of this wave
+    const int key = kw0 + col;            // this lane's key
+
+    const long long qoff = (long long)b * p.q_sb + (long long)h * p.q_sh;
+    const long long koff = (long long)b * p.k_sb + (long long)h * p.k_sh;
+    const char* qbase = (const char*)((const __bf16*)p.q + qoff);
+    const char* gbase = (const char*)((const __bf16*)p.dout + qoff);
+    const char* vbase = (const char*)((const __bf16*)p.v + koff + (long long)k0 * p.k_sn);
+    const unsigned qrb = (unsigned)(p.q_sn * 2), krb = (unsigned)(p.k_sn * 2);
+
+    // query tiles: causal keys >= k0 are seen only by queries >= k0
+    const int q_begin = CAUSAL ? k0 : 0;
+    const int n_qt = q_begin < Nq ? (Nq - q_begin + BQ - 1) / BQ : 0;
+
+    // K^T fragment (B operand of S = Q K^T): K[key][16kk + 8hi .. +7]
+    bf16x8 kreg[KK];
+    load_frag<D>(kreg, (const __bf16*)p.k + koff, p.k_sn, key, Nk, hi);
+
+    f32x16 dk[DB], dv[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dk[db][r] = dv[db][r] = 0.f;
+
+    lds_char* const lds = (lds_char*)smem;
+    lds_char* const vblk = lds;
+    lds_char* const qst = lds + VB_CH * 16;             // Q stage t at qst + t*QTB
+    lds_char* const gst = lds + VB_CH * 16 + 2 * QTB;   // dO stage t
+
+    // staging offsets (one per lane and tensor; see issue_tile)
+    unsigned ld_q, ld_v;
+    {
+        const int row = wave * (64 / DCH) + lane / DCH, ch = lane % DCH;
+        ld_q = row * qrb + kv_swz<D>(row, ch) * 16;
+        ld_v = row * krb + k_swz<D>(row, ch) * 16;
+    }
+    const unsigned long long qaddr = to_sgpr((unsigned long long)qbase);
+    const unsigned long long gaddr = to_sgpr((unsigned long long)gbase);
+    const int wofs = wave * 1024;   // this wave's part of a stage (bytes)
+#define FA_ISSUE_QG(t)                                                                                           \
+    do {                                                                                                         \
+        const int i0_ = q_begin + (t) * BQ;                                                                      \
+        issue_tile<LPWQ, DCH, BQ, NW>(qaddr + (unsigned long long)i0_ * qrb, qrb, ld_q, qst + ((t) & 1) * QTB + wofs, \
+                                      Nq - i0_, wave, lane);                                                     \
+        issue_tile<LPWQ, DCH, BQ, NW>(gaddr + (unsigned long long)i0_ * qrb, qrb, ld_q, gst + ((t) & 1) * QTB + wofs, \
+                                      Nq - i0_, wave, lane);                                                     \
+    } while (0)
+
+    // statistics of a query tile: lse * log2(e) and D (lanes 0..31 of wave 0)
+    const float* lse_bh = p.lse + (long long)bh * Nq;
+    const float* dl_bh = p.delta + (long long)bh * Nq;
+    float st_lse = 0.f, st_dl = 0.f;
+    auto load_stat = [&](int t) {
+        const int i = q_begin + t * BQ + lane;
+        st_lse = 0.f;
+        st_dl = 0.f;
+        if (wave == 0 && lane < BQ && i < Nq) {
+            st_lse = lse_bh[i] * kLog2e;
+            st_dl = dl_bh[i];
+        }
+    };
+    auto store_stat = [&](int t) {
+        if (wave == 0 && lane < BQ) {
+            stat[t & 1][0][lane] = st_lse;
+            stat[t & 1][1][lane] = st_dl;
+        }
+    };
+
+    // V^T fragment addressing (B operand of dP = dO V^T): V block row
+    // wave*32 + col, chunk 2kk + hi
+    const int vrow = wave * 32 + col;
+    // transposing-read addressing (see tr_times_packed)
+    const int tg = lane >> 4, ti = lane & 15;
+    const int tr_row = hi * 4 + (ti >> 2);
+    const int tr_dd = 16 * (tg & 1) + 4 * (ti & 3);
+    const float sl2 = p.scale_log2;
+
+    if (n_qt > 0) {
+        issue_tile<LPWV, DCH, BK, NW>(to_sgpr((unsigned long long)vbase), krb, ld_v, vblk + wofs, Nk - k0, wave,
+                                      lane);
+        FA_ISSUE_QG(0);
+        load_stat(0);
+    }
+    for (int t = 0; t < n_qt; ++t) {
+        const int i0 = q_begin + t * BQ;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        store_stat(t);
+        __syncthreads();
+        if (t + 1 < n_qt) {
+            FA_ISSUE_QG(t + 1);
+            load_stat(t + 1);
+        }
+        // a wave whose keys all lie after the tile's last query has nothing to add
+        if (CAUSAL && i0 + BQ - 1 < kw0) continue;
+
+        const u32x4* qs = (const u32x4*)(qst + (t & 1) * QTB);
+        const u32x4* gs = (const u32x4*)(gst + (t & 1) * QTB);
+        f32x16 s[1], dp[1];
+        rows_times_frag<D, 1, 2>(s, kreg, qs, col, hi);
+        // dP = dO V^T: A rows from the dO stage, B = V^T fragment from the V block
+        {
+            const u32x4* vb = (const u32x4*)vblk;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const u32x4 a = gs[col * DCH + kv_swz<D>(col, 2 * kk + hi)];
+                const u32x4 bv = vb[vrow * DCH + k_swz<D>(vrow, 2 * kk + hi)];
+                const f32x16 c = kk == 0 ? f32x16{} : dp[0];
+                dp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                __builtin_bit_cast(bf16x8, bv), c, 0, 0, 0);
+            }
+        }
+        // P = exp2(s*scale*log2e - lse2), dS = P (dP - D); masked pairs get 0
+        const bool masked = (CAUSAL && i0 < kw0 + 31) || i0 + BQ > Nq;
+        unsigned pkp[1][8], pks[1][8];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 l4 = *(const float4*)&stat[t & 1][0][g * 8 + hi * 4];
+            const float4 d4 = *(const float4*)&stat[t & 1][1][g * 8 + hi * 4];
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+            float pe[4], se[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][r], sl2, -lv[e]));
+                if (masked) {
+                    const int qi = i0 + g * 8 + hi * 4 + e;
+                    const bool vis = qi < Nq && (!CAUSAL || key <= qi);
+                    pr = vis ? pr : 0.f;
+                }
+                pe[e] = pr;
+                se[e] = pr * (dp[0][r] - dvv[e]);
+            }
+            pkp[0][2 * g + 0] = pack_bf16x2(pe[0], pe[1]);
+            pkp[0][2 * g + 1] = pack_bf16x2(pe[2], pe[3]);
+            pks[0][2 * g + 0] = pack_bf16x2(se[0], se[1]);
+            pks[0][2 * g + 1] = pack_bf16x2(se[2], se[3]);
+        }
+        tr_times_packed<D, 1>(dv, pkp, gst + (t & 1) * QTB, tr_row, tr_dd);
+        tr_times_packed<D, 1>(dk, pks, qst + (t & 1) * QTB, tr_row, tr_dd);
+    }
+#undef FA_ISSUE_QG
+
+    if (key < Nk) {
+        store_rows_f32<D>(p.dk + koff + (long long)key * p.k_sn, dk, p.scale, hi);
+        store_rows_f32<D>(p.dv + koff + (long long)key * p.k_sn, dv, 1.0f, hi);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ: query tiles outer.
+//
+// Register layout of one wave (32 queries; lane = (col, hi), col = the query):
+//   S^T, dP^T of a 64-key tile: s[kb][r] = key kb*32 + (r/4)*8 + hi*4 + r%4
+//   against query col;  dQ^T accumulator: acc[db][r] = d index
+//   db*32 + (r/4)*8 + hi*4 + r%4 of query col.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dq_kernel(BwdParams p) {
+    constexpr int NW = 8, BC = 64, BR = NW * 32, DCH = D / 8, KK = D / 16, DB = D / 32;
+    constexpr int TILE_CH = BC * DCH, TB = TILE_CH * 16, LPW = TILE_CH / 64 / NW;
+    static_assert(TILE_CH % (64 * NW) == 0, "tile must split evenly over the waves");
+
+    // K stages 0, 1 then V stages 0, 1
+    __shared__ u32x4 smem[4 * TILE_CH];
+
+    const int tid = __builtin_amdgcn_workitem_id_x();
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31;
+    const int hi = lane >> 5;
+
+    int bh, qt;
+    tile_of_block(__builtin_amdgcn_workgroup_id_x(), p.n_tiles, p.BH, CAUSAL, bh, qt);
+    const int b = bh / p.H;
+    const int h = bh - b * p.H;
+    const int Nq = p.Nq, Nk = p.Nk;
+    const int q_wg0 = qt * BR;
+    const int q_w0 = q_wg0 + wave * 32;
+    const int q = q_w0 + col;
+
+    const long long qoff = (long long)b * p.q_sb + (long long)h * p.q_sh;
+    const long long koff = (long long)b * p.k_sb + (long long)h * p.k_sh;
+    const unsigned krb = (unsigned)(p.k_sn * 2);
+
+    // key tiles: causal queries see keys <= query only
+    int kv_end = Nk;
+    if (CAUSAL) kv_end = min(Nk, min(q_wg0 + BR, Nq));
+    const int n_kt = (kv_end + BC - 1) / BC;
+    const int n_kt_wave = CAUSAL ? min(n_kt, (q_w0 + 31) / BC + 1) : n_kt;
+
+    bf16x8 qreg[KK], greg[KK];
+    load_frag<D>(qreg, (const __bf16*)p.q + qoff, p.q_sn, q, Nq, hi);
+    load_frag<D>(greg, (const __bf16*)p.dout + qoff, p.q_sn, q, Nq, hi);
+    float lse2 = 0.f, dlt = 0.f;
+    if (q < Nq) {
+        lse2 = p.lse[(long long)bh * Nq + q] * kLog2e;
+        dlt = p.delta[(long long)bh * Nq + q];
+    }
+
+    f32x16 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+    unsigned ld_k, ld_v;
+    {
+        const int row = wave * (64 / DCH) + lane / DCH, ch = lane % DCH;
+        ld_k = row * krb + kv_swz<D>(row, ch) * 16;
+        ld_v = row * krb + k_swz<D>(row, ch) * 16;
+    }
+    lds_char* const lds = (lds_char*)smem;
+    const unsigned long long kaddr = to_sgpr((unsigned long long)((const __bf16*)p.k + koff));
+    const unsigned long long vaddr = to_sgpr((unsigned long long)((const __bf16*)p.v + koff));
+    const unsigned long long tile_bytes = (unsigned long long)BC * krb;
+    lds_char* const ldst = lds + wave * 1024;
+#define FA_ISSUE_KV(t)                                                                                           \
+    do {                                                                                                         \
+        issue_tile<LPW, DCH, BC, NW>(kaddr + (unsigned long long)(t) * tile_bytes, krb, ld_k, ldst + ((t) & 1) * TB, \
+                                     Nk - (t) * BC, wave, lane);                                                 \
+        issue_tile<LPW, DCH, BC, NW>(vaddr + (unsigned long long)(t) * tile_bytes, krb, ld_v,                    \
+                                     ldst + (2 + ((t) & 1)) * TB, Nk - (t) * BC, wave, lane);                    \
+    } while (0)
+
+    const int tg = lane >> 4, ti = lane & 15;
+    const int tr_row = hi * 4 + (ti >> 2);
+    const int tr_dd = 16 * (tg & 1) + 4 * (ti & 3);
+    const float sl2 = p.scale_log2;
+
+    FA_ISSUE_KV(0);
+    for (int j = 0; j < n_kt; ++j) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (j + 1 < n_kt) FA_ISSUE_KV(j + 1);
+        if (j >= n_kt_wave) continue;
+
+        const lds_char* ks = lds + (j & 1) * TB;
+        const lds_char* vs = lds + (2 + (j & 1)) * TB;
+        f32x16 s[2], dp[2];
+        rows_times_frag<D, 2, 2>(s, qreg, (const u32x4*)ks, col, hi);
+        rows_times_frag<D, 2, 0>(dp, greg, (const u32x4*)vs, col, hi);
+        const int key0 = j * BC;
+        const bool masked = key0 + BC > Nk || (CAUSAL && key0 + BC - 1 > q_w0);
+        const int lim = (CAUSAL ? min(Nk - 1, q) : Nk - 1) - (key0 + hi * 4);
+        unsigned pk[2][8];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                float e2[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int r = 2 * jj + e;
+                    float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], sl2, -lse2));
+                    if (masked) pr = (kb * 32 + (r >> 2) * 8 + (r & 3)) <= lim ? pr : 0.f;
+                    e2[e] = pr * (dp[kb][r] - dlt);
+                }
+                pk[kb][jj] = pack_bf16x2(e2[0], e2[1]);
+            }
+        tr_times_packed<D, 2>(acc, pk, ks, tr_row, tr_dd);
+    }
+#undef FA_ISSUE_KV
+
+    if (q < Nq) store_rows_f32<D>(p.dq + qoff + (long long)q * p.q_sn, acc, p.scale, hi);
+}
+
+}  // namespace fa355
+
+using namespace fa355;
+
+namespace {
+
+bool aligned_b(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd(BwdParams p, bool o_bf16, long long n_rows, hipStream_t s) {
+    // 1. D = rowsum(dO * O)
+    const long long rpb = 256 / (D / 8);
+    const long long g1 = (n_rows + rpb - 1) / rpb;
+    if (o_bf16)
+        hipLaunchKernelGGL((fa_bwd_delta_kernel<D, true>), dim3((unsigned)g1), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((fa_bwd_delta_kernel<D, false>), dim3((unsigned)g1), dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // 2. dK, dV (128 keys per workgroup)
+    BwdParams p2 = p;
+    p2.n_tiles = (p.Nk + 127) / 128;
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((long long)p2.n_tiles * p.BH)), dim3(256), 0,
+                       s, p2);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // 3. dQ (256 queries per workgroup)
+    BwdParams p3 = p;
+    p3.n_tiles = (p.Nq + 255) / 256;
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((long long)p3.n_tiles * p.BH)), dim3(512), 0, s,
+                       p3);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, float* dq, float* dk, float* dv, float* delta,
+                            int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                            int layout, int in_dtype, int o_dtype, void* stream) {
+    // ---- validation: no HIP call before it passes
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (layout != FA_BHND && layout != FA_BSND) return FA_ERR_INVALID_ARG;
+    if (in_dtype != FA_BF16 && in_dtype != FA_F32) return FA_ERR_INVALID_ARG;
+    if (o_dtype != FA_BF16 && o_dtype != FA_F32) return FA_ERR_INVALID_ARG;
+    if (!aligned_b(q, 16) || !aligned_b(k, 16) || !aligned_b(v, 16) || !aligned_b(o, 16) || !aligned_b(dout, 16) ||
+        !aligned_b(dq, 16) || !aligned_b(dk, 16) || !aligned_b(dv, 16))
+        return FA_ERR_INVALID_ARG;
+    if (!aligned_b(lse, 4) || !aligned_b(delta, 4)) return FA_ERR_INVALID_ARG;
+    if (scale != scale || fabsf(scale) == INFINITY) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    const long long BH = (long long)B * H;
+    const long long n_rows = BH * Nq;
+    if (BH > INT32_MAX || n_rows / 16 > INT32_MAX || BH * ((Nk + 127) / 128) > INT32_MAX ||
+        BH * ((Nq + 255) / 256) > INT32_MAX)
+        return FA_ERR_UNSUPPORTED;
+    // tiles of up to 128 rows are addressed with 32-bit byte offsets
+    const long long row_bytes = (layout == FA_BSND ? (long long)H * d : (long long)d) * 2;
+    if (128 * row_bytes >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+
+    if (scale < 0.f) scale = 1.0f / sqrtf((float)d);
+
+    BwdParams p;
+    p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
+    p.dq = dq; p.dk = dk; p.dv = dv; p.delta = delta;
+    const long long D = d;
+    if (layout == FA_BHND) {
+        p.q_sb = (long long)H * Nq * D; p.q_sh = (long long)Nq * D; p.q_sn = D;
+        p.k_sb = (long long)H * Nk * D; p.k_sh = (long long)Nk * D; p.k_sn = D;
+    } else {
+        p.q_sb = (long long)Nq * H * D; p.q_sh = D; p.q_sn = (long long)H * D;
+        p.k_sb = (long long)Nk * H * D; p.k_sh = D; p.k_sn = (long long)H * D;
+    }
+    p.H = H; p.Nq = Nq; p.Nk = Nk;
+    p.n_tiles = 0;
+    p.BH = (int)BH;
+    p.scale = scale;
+    // scale 0 runs the exponentials with a tiny positive factor (every scaled
+    // score rounds away against the log-sum-exp, as with scale 0) and the
+    // gradients of Q and K are multiplied by the exact 0
+    p.scale_log2 = scale > 0.f ? scale * kLog2e : 1e-30f;
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool c = causal != 0, ob = o_dtype == FA_BF16;
+    hipError_t err;
+    if (d == 128) err = c ? launch_bwd<128, true>(p, ob, n_rows, s) : launch_bwd<128, false>(p, ob, n_rows, s);
+    else err = c ? launch_bwd<64, true>(p, ob, n_rows, s) : launch_bwd<64, false>(p, ob, n_rows, s);
+    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}

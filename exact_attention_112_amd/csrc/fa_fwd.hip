@@ -49,22 +49,10 @@
 #include <math.h>
 
 #include "fa355.h"
+#include "fa_common.h"
 
 namespace fa355 {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 // fp32 kernel: the running max moves only when a tile max exceeds it by more
 // than this (log2 units); probabilities then stay below 2^8 before the final
 // normalisation, which fp32 holds without loss.
@@ -83,75 +71,6 @@ struct FwdParams {
     int BH;                       // B * H
     float scale_log2;             // scale * log2(e)
 };
-
-// Workgroup id -> (batch*head, query tile).  Workgroups are dispatched round
-// robin over the 8 XCDs; when B*H is a multiple of 8, each XCD gets a
-// contiguous block of whole heads so one head's K/V stays in one XCD's L2.
-// Causal: heaviest (last) query tiles first.  A bijection in all cases.
-__device__ __forceinline__ void tile_of_block(int bid, int n_qtiles, int BH, bool causal,
-                                              int& bh, int& qt) {
-    if ((BH & 7) == 0) {
-        const int hpx = BH >> 3;
-        const int xcd = bid & 7;
-        const int s = bid >> 3;
-        if (causal) {
-            qt = n_qtiles - 1 - s / hpx;
-            bh = xcd * hpx + s % hpx;
-        } else {
-            bh = xcd * hpx + s / n_qtiles;
-            qt = s % n_qtiles;
-        }
-    } else if (causal) {
-        qt = n_qtiles - 1 - bid / BH;
-        bh = bid % BH;
-    } else {
-        bh = bid / n_qtiles;
-        qt = bid % n_qtiles;
-    }
-}
-
-// 16-byte-chunk swizzles of the LDS tiles (row = key within the tile, ch =
-// logical chunk of 8 bf16 along d).  K is read with ds_read_b128 by 32 lanes
-// on 32 consecutive rows at one chunk; V is read with ds_read_b64_tr_b16 on
-// 8 consecutive rows at 4 consecutive chunks.
-template <int D>
-__device__ __forceinline__ int k_swz(int row, int ch) {
-    if constexpr (D == 128) return ch ^ (row & 15);
-    else return ch ^ ((row >> 1) & 7);
-}
-template <int D>
-__device__ __forceinline__ int v_swz(int row, int ch) {
-    if constexpr (D == 128) return ch ^ ((row & 3) << 2);
-    else return ch ^ (((row >> 1) & 1) << 2);
-}
-
-__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
-    bf16x2 r = {(__bf16)a, (__bf16)b};   // v_cvt_pk_bf16_f32, round to nearest even
-    return __builtin_bit_cast(unsigned, r);
-}
-
-// x of this lane and x of the lane 32 apart, combined (every lane gets the
-// result for its pair).  v_permlane32_swap(a, b) exchanges lanes 32..63 of a
-// with lanes 0..31 of b; with a = b = x the two registers then hold x's low
-// half and x's high half, each in both halves.  Written as inline assembly:
-// the compiler's builtin for it returns the first register twice.  The
-// s_nop covers the VALU-write -> permlane-read hazard.
-__device__ __forceinline__ void swap_halves(float x, float& a, float& b) {
-    unsigned u = __builtin_bit_cast(unsigned, x), w = u;
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(u), "+v"(w));
-    a = __builtin_bit_cast(float, u);
-    b = __builtin_bit_cast(float, w);
-}
-__device__ __forceinline__ float pair_max(float x) {
-    float a, b;
-    swap_halves(x, a, b);
-    return fmaxf(a, b);
-}
-__device__ __forceinline__ float pair_sum(float x) {
-    float a, b;
-    swap_halves(x, a, b);
-    return a + b;
-}
 
 // ---------------------------------------------------------------------------
 // bf16 kernel
@@ -348,51 +267,6 @@ __device__ __forceinline__ void wave_step_serial(RowState<D>& st, f32x16 (&s)[2]
         qk_tile<D>(s, qreg, ks_nxt, col, hi);
         mask_tile<CAUSAL>(s, key0_nxt, q, Nk, hi);
         update_max(st, tile_max_scaled(s, sl2));
-    }
-}
-
-// One 16-byte-per-lane buffer load into LDS: lane i of the wave writes the
-// 16 bytes at rsrc + soff + voff (soff wave-uniform) to lds_dst + 16*i.
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, lds_char* lds_dst, unsigned voff,
-                                           unsigned soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_dst, 16, voff, (int)soff, 0, 0);
-}
-
-// A wave-uniform value moved to scalar registers (the compiler cannot always
-// prove uniformity on its own; a buffer descriptor must be scalar).
-__device__ __forceinline__ unsigned long long to_sgpr(unsigned long long a) {
-    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
-    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
-    return ((unsigned long long)hi << 32) | lo;
-}
-
-// Issue the loads of one K or V tile into an LDS stage.  Load j of wave w
-// fills tile rows j*RPL + w*RPW .. +RPW-1 (RPW = 64/DCH rows per wave load,
-// RPL = NW*RPW rows per round of loads), all DCH chunks of each.
-//   tile: address of the tile's first row (wave-uniform)
-//   off: this lane's byte offset inside the tile for load 0; load j adds the
-//        uniform j*RPL*rb (the swizzles repeat every 16 rows and RPL is a
-//        multiple of 16 whenever LPW > 1, so the chunk part is the same)
-//   dst: this wave's LDS chunks of load 0; load j adds j*RPL rows
-//   nvalid: rows of the tile inside the sequence (rows past it re-read the
-//        last valid row)
-template <int LPW, int DCH, int BC, int NW>
-__device__ __forceinline__ void issue_tile(unsigned long long tile, unsigned rb, unsigned off, lds_char* dst,
-                                           int nvalid, int wave, int lane) {
-    constexpr int RPW = 64 / DCH, RPL = NW * RPW;
-    static_assert(LPW == 1 || RPL % 16 == 0, "load rounds must keep the swizzle phase");
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)to_sgpr(tile), (short)0, (int)(BC * rb), 0x00020000);
-    if (nvalid >= BC) {
-#pragma unroll
-        for (int j = 0; j < LPW; ++j) load_lds16(rsrc, dst + j * RPL * DCH * 16, off, j * RPL * rb);
-    } else {
-#pragma unroll
-        for (int j = 0; j < LPW; ++j) {
-            const int row = j * RPL + wave * RPW + lane / DCH;
-            const unsigned o = off - (unsigned)(row - min(row, nvalid - 1)) * rb;
-            load_lds16(rsrc, dst + j * RPL * DCH * 16, o, j * RPL * rb);
-        }
     }
 }
 

@@ -1,6 +1,6 @@
 /*
- * fa355.h -- C ABI of libfa355, the attention forward pass for AMD Instinct
- * MI355X (gfx950).
+ * fa355.h -- C ABI of libfa355, the attention forward pass (and its backward
+ * pass, fa_bwd) for AMD Instinct MI355X (gfx950).
  *
  * The operation (pages cited by site: [nanhubrain] = nanhubrain.csdn.net,
  * FlashAttention in CANN ops-transformer; [pwwt] = www.pwwt.cn/news/2518640;
@@ -86,6 +86,52 @@ typedef enum fa_dtype {
  * deterministic: a fixed reduction order, no atomics.
  */
 FA355_API fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                           int layout, int in_dtype, int o_dtype, void* stream);
+
+/*
+ * fa_bwd -- enqueue the attention backward pass on `stream`: the gradients of
+ * a loss L with respect to Q, K and V, given dO = dL/dO.
+ *
+ * The operation ([nanhubrain] "backward recomputation"): the probabilities
+ * are rebuilt tile by tile from the forward pass's log-sum-exp,
+ * P_ij = exp(scale * q_i.k_j - LSE_i) on visible pairs (0 on masked ones), and
+ *   D_i  = sum_j P_ij (dO_i . v_j) = dO_i . O_i      (the whole row)
+ *   dS_ij = P_ij (dO_i . v_j - D_i)
+ *   dQ_i = scale * sum_j dS_ij k_j,   dK_j = scale * sum_i dS_ij q_i,
+ *   dV_j = sum_i P_ij dO_i.
+ * The page's listing sums the row term over one key block only; the softmax
+ * derivative needs it over the whole row, which is what is computed here.
+ *
+ * q, k, v   device pointers, as for fa_fwd (element type `in_dtype`).
+ * o         device pointer, the forward output O in Q's layout, element type
+ *           `o_dtype` (FA_F32 or FA_BF16); used only for D_i = dO_i . O_i.
+ * dout      device pointer, dO in Q's layout, element type `in_dtype`.
+ * lse       device pointer, float32 [B, H, Nq] contiguous: the natural-log
+ *           log-sum-exp of each row's scaled scores, as fa_fwd writes it.
+ * dq        device pointer, dQ written as float32 in Q's layout.
+ * dk, dv    device pointers, dK and dV written as float32 in K's layout.
+ * delta     device pointer to a caller-owned float32 workspace of B*H*Nq
+ *           elements; overwritten with D (its contents on entry do not
+ *           matter; on return it holds D_i in [B, H, Nq] order).
+ * B, H, Nq, Nk, d, scale, causal, layout: as for fa_fwd (scale < 0 selects
+ *           1/sqrt(d); scale must be the one the forward pass used).
+ * in_dtype  FA_BF16 (FA_F32 inputs return FA_ERR_UNSUPPORTED in this build).
+ * o_dtype   FA_F32 or FA_BF16.
+ * stream    a hipStream_t (NULL = the null stream).
+ *
+ * Alignment: q, k, v, o, dout, dq, dk, dv 16-byte aligned; lse and delta
+ * 4-byte aligned.  The outputs and the workspace must not overlap the inputs
+ * or each other.
+ *
+ * Ownership and asynchrony: as for fa_fwd.  The library allocates no device
+ * memory; the call validates its arguments (returning before any HIP call
+ * on failure), enqueues three kernels on `stream` (D, then dK/dV, then dQ)
+ * and returns without synchronising.  Results are deterministic: a fixed
+ * reduction order, no atomics.
+ */
+FA355_API fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, float* dq, float* dk, float* dv, float* delta,
                            int B, int H, int Nq, int Nk, int d, float scale, int causal,
                            int layout, int in_dtype, int o_dtype, void* stream);
 

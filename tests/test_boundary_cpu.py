@@ -118,3 +118,46 @@ def _load_fresh(path):
         fa.load(path)
     finally:
         fa._lib = saved
+
+
+BGOOD = dict(q=P, k=P + 0x1000, v=P + 0x2000, o=P + 0x3000, do=P + 0x5000, lse=P + 0x4000,
+             dq=P + 0x6000, dk=P + 0x7000, dv=P + 0x8000, delta=P + 0x9000, B=1, H=2, Nq=16, Nk=16,
+             d=64, scale=-1.0, causal=0, layout=fa.FA_BHND, in_dtype=fa.FA_BF16, o_dtype=fa.FA_F32,
+             stream=None)
+
+
+def bcall(**changes):
+    a = dict(BGOOD, **changes)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                     a["delta"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+                     a["layout"], a["in_dtype"], a["o_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("changes,status", [
+    *[(dict(**{name: 0}), fa.FA_ERR_INVALID_ARG)
+      for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "delta")],
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=-3), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(layout=5), fa.FA_ERR_INVALID_ARG),
+    (dict(in_dtype=3), fa.FA_ERR_INVALID_ARG),
+    (dict(o_dtype=9), fa.FA_ERR_INVALID_ARG),
+    (dict(do=P + 0x5008), fa.FA_ERR_INVALID_ARG),    # misaligned
+    (dict(dk=P + 0x7004), fa.FA_ERR_INVALID_ARG),
+    (dict(delta=P + 0x9002), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=math.nan), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-math.inf), fa.FA_ERR_INVALID_ARG),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(in_dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=1 << 16, H=1 << 16), fa.FA_ERR_UNSUPPORTED),
+])
+def test_bwd_validation_returns_before_launch(changes, status):
+    assert bcall(**changes) == status
+
+
+def test_bwd_python_wrapper_validates_without_gpu():
+    import torch
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    l = torch.zeros(1, 1, 4)
+    with pytest.raises(ValueError):
+        fa.bwd(x, x, x, x, x, l)               # CPU tensors are refused
