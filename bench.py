@@ -1,6 +1,7 @@
-"""Benchmark of the attention forward pass on one MI355X.
+"""Benchmark of the attention forward pass (default) or backward pass on one
+MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd]
 
 One step = one call of the HIP forward kernel (the whole hot path: Q tile
 load, K/V staging, S = Q K^T, mask, online softmax, P V, epilogue) over the
@@ -14,6 +15,12 @@ throughput in TFLOP/s (4*B*H*Nq*Nk*d, halved for causal) and:
 * cpu_baseline: the fp64 CPU oracle timed on this host's cores on a bounded
   sample of the same workload (rows of the first heads, about 10 s of work),
   as a reported baseline, not a target.
+
+With ``--pass bwd`` one step is one fa_bwd call (D = rowsum(dO*O), the dK/dV
+kernel and the dQ kernel) on the workload, given O and LSE from one forward
+call made before the timed region; the throughput counts the backward's five
+products, 2.5x the forward's flops (10*B*H*Nq*Nk*d, halved for causal), and
+the roofline is that of the whole call.
 """
 from __future__ import annotations
 
@@ -29,9 +36,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOPS and % of bf16 MFMA peak at B4 H32 N8192 d128"
+BWD_METRIC = "attention bwd TFLOPS and % of bf16 MFMA peak at B4 H32 N8192 d128"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA (published)
 PEAK_F32_TFLOPS = 157.3            # MI355X fp32 (matrix and vector), published
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
+
+
+def bwd_algorithmic_bytes(w) -> float:
+    """Read Q, K, V, dO (bf16), O (fp32) and LSE once; write dQ, dK, dV (fp32) once."""
+    per_head = (2 * w.Nq + 2 * w.Nk) * w.d * 2 + w.Nq * w.d * 4 + w.Nq * 4 + (w.Nq + 2 * w.Nk) * w.d * 4
+    return float(per_head) * w.B * w.H
 
 
 def algorithmic_bytes(w, out_bytes: int) -> float:
@@ -41,29 +55,32 @@ def algorithmic_bytes(w, out_bytes: int) -> float:
     return float(per_head) * w.B * w.H
 
 
-# the forward kernel's sources (its file and the shared device header)
-KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_112_amd", "csrc", n) for n in ("fa_fwd.hip", "fa_common.h")]
+# the kernels' sources (their file and the shared device header)
+KERNEL_SOURCES = {
+    p: [os.path.join(ROOT, "exact_attention_112_amd", "csrc", n) for n in (f"fa_{p}.hip", "fa_common.h")]
+    for p in ("fwd", "bwd")
+}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(which: str = "fwd") -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in KERNEL_SOURCES[which]:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str):
-    """HBM bytes per launch from profiles/<...>_counters.md, if the summary was
-    taken on the current kernel source; else None."""
-    path = os.path.join(PROFILES, f"fa_fwd_{workload}_counters.md")
+def traffic_from_profiles(workload: str, which: str = "fwd"):
+    """HBM bytes per launch from profiles/fa_<which>_<workload>_counters.md, if
+    the summary was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"fa_{which}_{workload}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash(which):
         return None
     return float(m_bytes.group(1))
 
@@ -111,6 +128,45 @@ def cpu_baseline(w, inp, target_s: float = 10.0):
     }
 
 
+def cpu_baseline_bwd(w, inp, grad, target_s: float = 10.0):
+    """Time the fp64 backward oracle head by head (in (b, h) order) until at
+    least ``target_s`` seconds of work are done: per head, the row statistics
+    of every query plus dQ of every 4th query row and dK, dV of every 4th key
+    row.  The rate counts the algorithmic backward flops of the rows returned
+    (dQ is 2 of the backward's 5 products, dK and dV 3 of them)."""
+    import numpy as np
+    import oracle
+
+    lib = oracle.lib()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or lib.max_threads()
+    qrows = np.arange(0, w.Nq, 4, dtype=np.int32)
+    krows = np.arange(0, w.Nk, 4, dtype=np.int32)
+    per_head = 2.5 * 4.0 * w.Nq * w.Nk * w.d * (0.5 if w.causal else 1.0)
+    frac = 0.4 * len(qrows) / w.Nq + 0.6 * len(krows) / w.Nk
+    done, elapsed = 0, 0.0
+    while done < w.B * w.H and elapsed < target_s:
+        b, h = divmod(done, w.H)
+        if w.layout == "BHND":
+            sl = lambda x: x[b:b + 1, h:h + 1]
+        else:
+            sl = lambda x: x[b:b + 1, :, h:h + 1]
+        t0 = time.perf_counter()
+        lib.attn_bwd(sl(inp.q), sl(inp.k), sl(inp.v), sl(grad), scale=w.scale, causal=w.causal,
+                     layout=w.layout, qrows=qrows, krows=krows, n_threads=threads)
+        elapsed += time.perf_counter() - t0
+        done += 1
+    flops = done * per_head * frac
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fp64 backward oracle on the first {done} of {w.B * w.H} heads of {w.name}: row "
+                   f"statistics of all {w.Nq} queries, dQ of every 4th query row, dK and dV of every 4th "
+                   f"key row; {flops:.3e} algorithmic flop in {elapsed:.1f} s on {threads} threads"),
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +174,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="selfattn_b4h32n8k")
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
+                    help="time the forward pass (default) or the backward pass")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -164,6 +222,22 @@ def main(argv=None):
         fa.fwd(tq, tk, tv, causal=w.causal, scale=w.scale, layout=w.layout, out_dtype=out_dtype,
                out=o, lse=lse)
 
+    if args.which == "bwd":
+        if w.dtype != "bf16":
+            print("bench.py: the backward pass takes bf16 inputs", file=sys.stderr)
+            return 2
+        grad_vals, grad_bits = I.make_grad(w)
+        tdo = up(grad_bits)
+        step()                                   # O and LSE for the backward, untimed
+        dq = torch.empty(tq.shape, dtype=torch.float32, device="cuda")
+        dk = torch.empty(tk.shape, dtype=torch.float32, device="cuda")
+        dv = torch.empty(tk.shape, dtype=torch.float32, device="cuda")
+        delta = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+
+        def step():  # noqa: F811  (the timed step of the backward benchmark)
+            fa.bwd(tq, tk, tv, o, tdo, lse, causal=w.causal, scale=w.scale, layout=w.layout,
+                   dq=dq, dk=dk, dv=dv, delta=delta)
+
     print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -178,20 +252,23 @@ def main(argv=None):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    tflops = w.flops / (ms * 1e-3) / 1e12
-    if not (torch.isfinite(o).all() and torch.isfinite(lse).all()):
+    bwd = args.which == "bwd"
+    flops = 2.5 * w.flops if bwd else w.flops
+    tflops = flops / (ms * 1e-3) / 1e12
+    outs = (dq, dk, dv) if bwd else (o, lse)
+    if not all(torch.isfinite(t).all() for t in outs):
         print("bench: non-finite output", file=sys.stderr)
         return 1
 
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, inp)
+        cpu = cpu_baseline_bwd(w, inp, grad_vals) if bwd else cpu_baseline(w, inp)
 
-    traffic = traffic_from_profiles(w.name)
+    traffic = traffic_from_profiles(w.name, args.which)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    nbytes = algorithmic_bytes(w, 2 if args.out_dtype == "bf16" else 4)
-    if w.flops / nbytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+    nbytes = bwd_algorithmic_bytes(w) if bwd else algorithmic_bytes(w, 2 if args.out_dtype == "bf16" else 4)
+    if flops / nbytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9):
         gbs = nbytes / (ms * 1e-3) / 1e9     # below the ridge point: HBM-bound
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
@@ -199,7 +276,7 @@ def main(argv=None):
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(tflops / peak, 4), "traffic": traffic}
     line = {
-        "metric": METRIC,
+        "metric": BWD_METRIC if bwd else METRIC,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -210,9 +287,11 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded N(0,1) Q/K/V of the workload's shape)",
+        "data": ("synthetic (seeded N(0,1) Q/K/V/dO of the workload's shape; O, LSE from the GPU forward)"
+                 if bwd else "synthetic (seeded N(0,1) Q/K/V of the workload's shape)"),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
-                   "causal": w.causal, "layout": w.layout, "out_dtype": args.out_dtype},
+                   "causal": w.causal, "layout": w.layout, "out_dtype": args.out_dtype,
+                   **({"pass": "bwd", "grads": "f32"} if bwd else {})},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
