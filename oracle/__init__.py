@@ -6,7 +6,7 @@ Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 it shares no code with the GPU path (the only common module is the seeded
 input generator, which holds none of the method's arithmetic).
 
-Three implementations live here:
+Four implementations live here:
 
 * ``attn_fwd`` -- the plain definition, a two-pass fp64 softmax attention in C
   (``oracle.c``): scores, row max, exp-sum, weighted sum of values, one row at
@@ -19,6 +19,11 @@ Three implementations live here:
   P, dP = dO V^T, D_i = rowsum(P * dP) over the whole row, dS = P * (dP - D),
   dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO ([nanhubrain] "backward
   recomputation", with the row term taken over the whole row).
+* ``attn_fwd_ex`` -- the forward with grouped key/value heads (GQA/MQA:
+  query head h reads KV head h // (H // Hkv), [nanhubrain] "GatherPAKVCache")
+  and a band of visible keys i-left <= j <= i+right ([pwwt] "standard vs
+  IO-aware": pre_tokens / next_tokens), plain fp64 C; a row with no visible
+  key gives O = 0, LSE = -inf.
 * ``online.attn_fwd_online`` -- the pages' own algorithm, the tiled forward
   with the online-softmax recurrence ([nanhubrain] "tiling skeleton",
   [ascendai] section 2.2), in numpy fp64, over caller-chosen block splits.
@@ -74,6 +79,10 @@ class OracleLib:
         h.restype = _c_int
         h.argtypes = ([_c_ptr] * 4 + [_c_i64] * 6 + [_c_int] * 5 + [_c_dbl, _c_int]
                       + [_c_ptr, _c_int, _c_ptr, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_int])
+        x = self._lib.oracle_attn_fwd_ex
+        x.restype = _c_int
+        x.argtypes = ([_c_ptr] * 3 + [_c_i64] * 6 + [_c_int] * 6 + [_c_dbl] + [_c_int] * 3
+                      + [_c_ptr, _c_int, _c_ptr, _c_ptr, _c_int])
         self._lib.oracle_max_threads.restype = _c_int
 
     def max_threads(self) -> int:
@@ -172,6 +181,48 @@ class OracleLib:
             raise RuntimeError(f"oracle_attn_bwd failed with code {rc}")
         return dq, dk, dv
 
+    def attn_fwd_ex(self, q, k, v, *, scale: float, causal: bool = False, window=(-1, -1),
+                    layout: str = "BHND", rows=None, n_threads: int = 0):
+        """O [B,H,R,d] and LSE [B,H,R] (float64) with grouped KV heads and a band.
+
+        q: [B,H,Nq,d] (BHND) or [B,Nq,H,d] (BSND); k, v: the same with Nk and
+        Hkv heads (H % Hkv == 0; query head h reads KV head h // (H // Hkv)).
+        window = (left, right): key j visible to query i iff i-left <= j <=
+        i+right (a negative bound is unbounded), and j <= i if causal.  Rows
+        with no visible key give O = 0 and LSE = -inf.
+        """
+        q = np.ascontiguousarray(q, dtype=np.float32)
+        k = np.ascontiguousarray(k, dtype=np.float32)
+        v = np.ascontiguousarray(v, dtype=np.float32)
+        if k.shape != v.shape:
+            raise ValueError("k and v must have the same shape")
+        if layout == "BHND":
+            B, H, Nq, d = q.shape
+            Hkv, Nk = k.shape[1], k.shape[2]
+            qs = (H * Nq * d, Nq * d, d)
+            ks = (Hkv * Nk * d, Nk * d, d)
+        elif layout == "BSND":
+            B, Nq, H, d = q.shape
+            Nk, Hkv = k.shape[1], k.shape[2]
+            qs = (Nq * H * d, d, H * d)
+            ks = (Nk * Hkv * d, d, Hkv * d)
+        else:
+            raise ValueError(f"unknown layout {layout!r}")
+        if rows is None:
+            R, rows_arr, rows_ptr = Nq, None, None
+        else:
+            rows_arr = np.ascontiguousarray(rows, dtype=np.int32)
+            R, rows_ptr = int(rows_arr.size), rows_arr.ctypes.data
+        o = np.empty((B, H, R, d), dtype=np.float64)
+        lse = np.empty((B, H, R), dtype=np.float64)
+        rc = self._lib.oracle_attn_fwd_ex(
+            q.ctypes.data, k.ctypes.data, v.ctypes.data, *qs, *ks, B, H, Hkv, Nq, Nk, d,
+            float(scale), int(bool(causal)), int(window[0]), int(window[1]),
+            rows_ptr, R, o.ctypes.data, lse.ctypes.data, int(n_threads))
+        if rc != 0:
+            raise RuntimeError(f"oracle_attn_fwd_ex failed with code {rc}")
+        return o, lse
+
     def attn_probs(self, q, k, *, scale: float, causal: bool = False):
         """P [Nq, Nk] (float64) of one head; q [Nq,d], k [Nk,d] float32."""
         q = np.ascontiguousarray(q, dtype=np.float32)
@@ -210,3 +261,7 @@ def attn_probs(q, k, **kw):
 
 def attn_bwd(q, k, v, do, **kw):
     return lib().attn_bwd(q, k, v, do, **kw)
+
+
+def attn_fwd_ex(q, k, v, **kw):
+    return lib().attn_fwd_ex(q, k, v, **kw)

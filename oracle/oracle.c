@@ -339,3 +339,103 @@ int oracle_attn_bwd(const float* q, const float* k, const float* v, const float*
     free(stat);
     return status;
 }
+
+/* ------------------------------------------------------------------------
+ * Extended forward: grouped key/value heads and a band of visible keys, in
+ * double.
+ *
+ * Visible keys of query i: lo_i <= j <= hi_i with
+ *   lo_i = max(0, i - window_left)            (window_left < 0: lo_i = 0)
+ *   hi_i = min(Nk - 1, i + window_right)      (window_right < 0: Nk - 1)
+ * and, if causal, hi_i <= i as well.  This is the band of [pwwt] "standard vs
+ * IO-aware" (`pre_tokens` keys before the query, `next_tokens` after it;
+ * causal = next_tokens 0).  Query head h reads key/value head h / (H / Hkv):
+ * the grouped (GQA) and multi-query (MQA, Hkv = 1) head maps of [nanhubrain]
+ * "GatherPAKVCache" (only the needed KV heads are read).  A row with no
+ * visible key has an empty softmax: O = 0 and LSE = -inf (the log of an
+ * empty sum).
+ * ---------------------------------------------------------------------- */
+
+/* One query row over keys [lo, hi] (lo <= hi): scores, max, exp-sum, weighted
+ * sum of value rows, all in double; `s` is scratch of Nk doubles. */
+static void band_row(const float* qi, const float* kbh, const float* vbh, int64_t kv_sn,
+                     int lo, int hi, int d, double scale, double* s, double* out_o, double* out_lse)
+{
+    double top = -INFINITY;
+    for (int j = lo; j <= hi; ++j) {
+        const float* kj = kbh + (int64_t)j * kv_sn;
+        double acc = 0.0;
+        for (int c = 0; c < d; ++c) acc += (double)qi[c] * (double)kj[c];
+        s[j] = scale * acc;
+        if (s[j] > top) top = s[j];
+    }
+    double z = 0.0;
+    for (int c = 0; c < d; ++c) out_o[c] = 0.0;
+    for (int j = lo; j <= hi; ++j) {
+        const double w = exp(s[j] - top);
+        z += w;
+        const float* vrow = vbh + (int64_t)j * kv_sn;
+        for (int c = 0; c < d; ++c) out_o[c] += w * (double)vrow[c];
+    }
+    for (int c = 0; c < d; ++c) out_o[c] /= z;
+    *out_lse = top + log(z);
+}
+
+/*
+ * oracle_attn_fwd_ex: O [B,H,R,d] and LSE [B,H,R] in double for queries with H
+ * heads and keys/values with Hkv heads (H % Hkv == 0; K/V strides describe the
+ * Hkv-head tensors), under the band (window_left, window_right; negative =
+ * unbounded) and the causal flag.  Rows as in oracle_attn_fwd.  Returns 0, -1
+ * on bad arguments, -2 on allocation failure.
+ */
+int oracle_attn_fwd_ex(const float* q, const float* k, const float* v,
+                       int64_t q_sb, int64_t q_sh, int64_t q_sn,
+                       int64_t kv_sb, int64_t kv_sh, int64_t kv_sn,
+                       int B, int H, int Hkv, int Nq, int Nk, int d,
+                       double scale, int causal, int window_left, int window_right,
+                       const int32_t* rows, int n_rows,
+                       double* o, double* lse, int n_threads)
+{
+    if (!q || !k || !v || !o || !lse) return -1;
+    if (B < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 || Nq < 1 || Nk < 1 || d < 1) return -1;
+    const int R = rows ? n_rows : Nq;
+    if (R < 1) return -1;
+    for (int r = 0; rows && r < R; ++r)
+        if (rows[r] < 0 || rows[r] >= Nq) return -1;
+    if (n_threads <= 0) n_threads = omp_get_max_threads();
+    const int group = H / Hkv;
+
+    int status = 0;
+    const int64_t total = (int64_t)B * H * R;
+#pragma omp parallel num_threads(n_threads)
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)Nk);
+        if (!s) {
+#pragma omp atomic write
+            status = -2;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t t = 0; t < total; ++t) {
+            if (!s) continue;
+            const int64_t bh = t / R;
+            const int r = (int)(t % R);
+            const int b = (int)(bh / H), h = (int)(bh % H), hk = h / group;
+            const int i = rows == NULL ? r : rows[r];
+            int lo = 0, hi = Nk - 1;
+            if (window_left >= 0 && i - window_left > lo) lo = i - window_left;
+            if (window_right >= 0 && (int64_t)i + window_right < hi) hi = i + window_right;
+            if (causal && i < hi) hi = i;
+            double* out_o = o + t * d;
+            if (lo > hi) {
+                for (int c = 0; c < d; ++c) out_o[c] = 0.0;
+                lse[t] = -INFINITY;
+                continue;
+            }
+            const float* qi = q + (int64_t)b * q_sb + (int64_t)h * q_sh + (int64_t)i * q_sn;
+            const int64_t kvoff = (int64_t)b * kv_sb + (int64_t)hk * kv_sh;
+            band_row(qi, k + kvoff, v + kvoff, kv_sn, lo, hi, d, scale, s, out_o, lse + t);
+        }
+        free(s);
+    }
+    return status;
+}
