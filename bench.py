@@ -49,10 +49,11 @@ def bwd_algorithmic_bytes(w) -> float:
 
 
 def algorithmic_bytes(w, out_bytes: int) -> float:
-    """Read Q, K, V once, write O and LSE once (per launch)."""
+    """Read Q, K, V once (K and V have w.kv_heads heads), write O and LSE once (per launch)."""
     el = 2 if w.dtype == "bf16" else 4
-    per_head = (w.Nq + 2 * w.Nk) * w.d * el + w.Nq * w.d * out_bytes + w.Nq * 4
-    return float(per_head) * w.B * w.H
+    q_side = w.H * (w.Nq * w.d * el + w.Nq * w.d * out_bytes + w.Nq * 4)
+    kv_side = w.kv_heads * 2 * w.Nk * w.d * el
+    return float(q_side + kv_side) * w.B
 
 
 # the kernels' sources (their file and the shared device header)
@@ -97,24 +98,36 @@ def cpu_baseline(w, inp, target_s: float = 10.0):
     heads_per_chunk = 2
     done_heads, flops, elapsed = 0, 0.0, 0.0
     total_heads = w.B * w.H
+    extended = w.kv_heads != w.H or w.window != (-1, -1)
+    group = w.H // w.kv_heads
+
+    def n_visible(i):
+        lo = max(0, i - w.window[0]) if w.window[0] >= 0 else 0
+        hi = min(w.Nk - 1, i + w.window[1]) if w.window[1] >= 0 else w.Nk - 1
+        if w.causal:
+            hi = min(hi, i)
+        return max(0, hi - lo + 1)
+
+    per_head = float(sum(4.0 * n_visible(int(r)) * w.d for r in rows))
     while done_heads < total_heads and elapsed < target_s:
         n = min(heads_per_chunk, total_heads - done_heads)
         sl = []
         for t in range(done_heads, done_heads + n):
             b, h = divmod(t, w.H)
+            hk = h // group
             if w.layout == "BHND":
-                sl.append((inp.q[b:b + 1, h:h + 1], inp.k[b:b + 1, h:h + 1], inp.v[b:b + 1, h:h + 1]))
+                sl.append((inp.q[b:b + 1, h:h + 1], inp.k[b:b + 1, hk:hk + 1], inp.v[b:b + 1, hk:hk + 1]))
             else:
-                sl.append((inp.q[b:b + 1, :, h:h + 1], inp.k[b:b + 1, :, h:h + 1], inp.v[b:b + 1, :, h:h + 1]))
+                sl.append((inp.q[b:b + 1, :, h:h + 1], inp.k[b:b + 1, :, hk:hk + 1], inp.v[b:b + 1, :, hk:hk + 1]))
         t0 = time.perf_counter()
         for q, k, v in sl:
-            lib.attn_fwd(q, k, v, scale=w.scale, causal=w.causal, layout=w.layout, rows=rows,
-                         n_threads=threads)
+            if extended:
+                lib.attn_fwd_ex(q, k, v, scale=w.scale, causal=w.causal, window=w.window, layout=w.layout,
+                                rows=rows, n_threads=threads)
+            else:
+                lib.attn_fwd(q, k, v, scale=w.scale, causal=w.causal, layout=w.layout, rows=rows,
+                             n_threads=threads)
         elapsed += time.perf_counter() - t0
-        if w.causal:
-            per_head = float(sum(4.0 * min(int(r) + 1, w.Nk) * w.d for r in rows))
-        else:
-            per_head = 4.0 * len(rows) * w.Nk * w.d
         flops += n * per_head
         done_heads += n
     return {
@@ -220,11 +233,12 @@ def main(argv=None):
 
     def step():
         fa.fwd(tq, tk, tv, causal=w.causal, scale=w.scale, layout=w.layout, out_dtype=out_dtype,
-               out=o, lse=lse)
+               out=o, lse=lse, window=None if w.window == (-1, -1) else w.window)
 
     if args.which == "bwd":
-        if w.dtype != "bf16":
-            print("bench.py: the backward pass takes bf16 inputs", file=sys.stderr)
+        if w.dtype != "bf16" or w.kv_heads != w.H or w.window != (-1, -1):
+            print("bench.py: the backward pass takes bf16 inputs, one KV head per query head and no band",
+                  file=sys.stderr)
             return 2
         grad_vals, grad_bits = I.make_grad(w)
         tdo = up(grad_bits)
@@ -276,7 +290,8 @@ def main(argv=None):
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(tflops / peak, 4), "traffic": traffic}
     line = {
-        "metric": BWD_METRIC if bwd else METRIC,
+        "metric": ((BWD_METRIC if bwd else METRIC) if w.name == "selfattn_b4h32n8k"
+                   else f"attention {args.which} TFLOPS and % of bf16 MFMA peak at {w.name}"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -291,6 +306,8 @@ def main(argv=None):
                  if bwd else "synthetic (seeded N(0,1) Q/K/V of the workload's shape)"),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                    "causal": w.causal, "layout": w.layout, "out_dtype": args.out_dtype,
+                   **({"Hkv": w.kv_heads, "window": list(w.window)}
+                      if w.kv_heads != w.H or w.window != (-1, -1) else {}),
                    **({"pass": "bwd", "grads": "f32"} if bwd else {})},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -34,7 +34,7 @@ FA_BF16, FA_F32 = 0, 1
 LAYOUTS = {"BHND": FA_BHND, "BSND": FA_BSND}
 
 # the symbols include/fa355.h declares
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_status_str", "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_status_str", "fa_abi_version")
 ABI_VERSION = 1
 
 _lib = None
@@ -69,6 +69,9 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.fa_fwd.restype = ctypes.c_int
     lib.fa_fwd.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_float]
                            + [ctypes.c_int] * 4 + [ctypes.c_void_p])
+    lib.fa_fwd_ex.restype = ctypes.c_int
+    lib.fa_fwd_ex.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [ctypes.c_float]
+                              + [ctypes.c_int] * 6 + [ctypes.c_void_p])
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float]
                            + [ctypes.c_int] * 4 + [ctypes.c_void_p])
@@ -94,14 +97,26 @@ def fa_fwd(q: int, k: int, v: int, o: int, lse: int | None, B: int, H: int, Nq: 
                              int(causal), int(layout), int(in_dtype), int(o_dtype), stream or None))
 
 
+def fa_fwd_ex(q: int, k: int, v: int, o: int, lse: int | None, B: int, H: int, Hkv: int, Nq: int, Nk: int,
+              d: int, scale: float, causal: int, window_left: int, window_right: int, layout: int,
+              in_dtype: int, o_dtype: int, stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the fa_status."""
+    return int(load().fa_fwd_ex(q, k, v, o, lse or None, B, H, Hkv, Nq, Nk, d, float(scale), int(causal),
+                                int(window_left), int(window_right), int(layout), int(in_dtype),
+                                int(o_dtype), stream or None))
+
+
 def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, layout: str = "BHND",
-        out_dtype=None, out=None, lse=None, return_lse: bool = True):
+        out_dtype=None, out=None, lse=None, return_lse: bool = True, window=None):
     """Attention forward on torch CUDA tensors (ROCm).
 
-    q: [B,H,Nq,d] (BHND) or [B,Nq,H,d] (BSND); k, v: same with Nk.  bf16 or
-    fp32, contiguous, on one GPU.  Returns (O, LSE): O in q's layout with
-    dtype ``out_dtype`` (default float32), LSE float32 [B,H,Nq].  The kernel
-    is enqueued on the current stream.
+    q: [B,H,Nq,d] (BHND) or [B,Nq,H,d] (BSND); k, v: same with Nk and Hkv
+    heads, Hkv dividing H (grouped-query attention when Hkv < H).  bf16 or
+    fp32, contiguous, on one GPU.  ``window=(left, right)``: key j visible to
+    query i iff i-left <= j <= i+right (a negative side is unbounded).
+    Returns (O, LSE): O in q's layout with dtype ``out_dtype`` (default
+    float32), LSE float32 [B,H,Nq].  The kernel is enqueued on the current
+    stream.
     """
     import torch
 
@@ -125,8 +140,9 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, layout: st
     else:
         B, Nq, H, d = q.shape
         Bk, Nk, Hk, dk = k.shape
-    if (Bk, Hk, dk) != (B, H, d):
+    if Bk != B or dk != d or Hk < 1 or H % Hk != 0:
         raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree for layout {layout}")
+    wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("out_dtype must be float32 or bfloat16")
@@ -143,10 +159,14 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, layout: st
     o_dt = FA_BF16 if out_dtype == torch.bfloat16 else FA_F32
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
-        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                    lse.data_ptr() if lse is not None else None, B, H, Nq, Nk, d,
-                    -1.0 if scale is None else float(scale), int(bool(causal)), LAYOUTS[layout],
-                    in_dt, o_dt, stream)
+        sc = -1.0 if scale is None else float(scale)
+        lp = lse.data_ptr() if lse is not None else None
+        if Hk == H and wl < 0 and wr < 0:
+            st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lp, B, H, Nq, Nk, d,
+                        sc, int(bool(causal)), LAYOUTS[layout], in_dt, o_dt, stream)
+        else:
+            st = fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lp, B, H, Hk, Nq, Nk, d,
+                           sc, int(bool(causal)), wl, wr, LAYOUTS[layout], in_dt, o_dt, stream)
     if st == FA_ERR_INVALID_ARG:
         raise FaInvalidArgument(st, "invalid argument")
     if st == FA_ERR_UNSUPPORTED:

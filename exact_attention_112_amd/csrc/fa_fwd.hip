@@ -70,6 +70,8 @@ struct FwdParams {
     int n_qtiles;                 // ceil(Nq / rows per workgroup)
     int BH;                       // B * H
     float scale_log2;             // scale * log2(e)
+    int group;                    // query heads per key/value head (H / Hkv)
+    int wl, wr;                   // band: keys i-wl .. i+wr visible (negative: unbounded)
 };
 
 // ---------------------------------------------------------------------------
@@ -120,6 +122,20 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int key0, int q, int N
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             s[kb][r] = (kb * 32 + (r >> 2) * 8 + (r & 3)) <= lim ? s[kb][r] : -INFINITY;
+}
+
+// Band mask: key j is visible to this lane's query iff lo <= j <= hi (lane
+// constants: lo = i - wl or no bound, hi = min(Nk-1, i + wr, causal ? i)).
+__device__ __forceinline__ void mask_tile_band(f32x16 (&s)[2], int key0, int lo, int hi_key, int hi) {
+    const int base = key0 + hi * 4;
+    const int lo_r = lo - base, hi_r = hi_key - base;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+            s[kb][r] = (off >= lo_r && off <= hi_r) ? s[kb][r] : -INFINITY;
+        }
 }
 
 // Row max of the tile, scaled to log2 units (the scale is > 0, so the max of
@@ -187,12 +203,15 @@ __device__ __forceinline__ void pv_tile(f32x16 (&oacc)[D / 32], const unsigned (
 // Move the running max to include a new tile whose scaled row max is mt2.
 // The rescale by alpha = exp2(m_old - m_new) is skipped by the whole wave when
 // no row's max moved (alpha would be 1 for every lane).
-template <int D>
+// SAFE: a row may have seen no visible key yet (m = -inf), so alpha is taken
+// as 1 where the max did not move instead of exp2(-inf - -inf).
+template <int D, bool SAFE = false>
 __device__ __forceinline__ void update_max(RowState<D>& st, float mt2) {
     const bool move = mt2 > st.m;
     if (__builtin_amdgcn_ballot_w64(move)) {
         const float m_new = move ? mt2 : st.m;
-        const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+        float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+        if constexpr (SAFE) alpha = move ? alpha : 1.0f;
         st.l0 *= alpha;
         st.l1 *= alpha;
 #pragma unroll
@@ -270,6 +289,23 @@ __device__ __forceinline__ void wave_step_serial(RowState<D>& st, f32x16 (&s)[2]
     }
 }
 
+// The serial step under a band: rows may have no visible key so far (m =
+// -inf), so the exponent uses a finite stand-in for m (every score of such a
+// row is -inf and still gives 0) and the max update is the safe one.
+template <int D, bool HAS_NXT>
+__device__ __forceinline__ void wave_step_band(RowState<D>& st, f32x16 (&s)[2], const bf16x8 (&qreg)[D / 16],
+                                               const u32x4* ks_nxt, const lds_char* vs_cur, int key0_nxt, int lo,
+                                               int hi_key, float sl2, int col, int hi, int tr_row, int tr_dd) {
+    unsigned pk[2][8];
+    tile_exp(s, fmaxf(st.m, -3.0e38f), sl2, pk, st.l0, st.l1);
+    pv_tile<D>(st.oacc, pk, vs_cur, tr_row, tr_dd);
+    if constexpr (HAS_NXT) {
+        qk_tile<D>(s, qreg, ks_nxt, col, hi);
+        mask_tile_band(s, key0_nxt, lo, hi_key, hi);
+        update_max<D, true>(st, tile_max_scaled(s, sl2));
+    }
+}
+
 template <int D, int NW>
 struct Bf16Cfg {
     static constexpr int BC = 64;                 // keys per tile
@@ -281,7 +317,10 @@ struct Bf16Cfg {
     static_assert(TILE_CH % (64 * NW) == 0, "tile must split evenly over the waves");
 };
 
-template <int D, int NW, bool CAUSAL, bool OUT_BF16>
+// BAND: keys outside the band i-wl .. i+wr are masked and the tiles outside
+// the workgroup's band are never loaded; rows may see no key at all (O = 0,
+// LSE = -inf).
+template <int D, int NW, bool CAUSAL, bool OUT_BF16, bool BAND>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_kernel(FwdParams p) {
     using C = Bf16Cfg<D, NW>;
@@ -307,24 +346,55 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     const int q = q_w0 + col;             // this lane's query
     const int Nq = p.Nq, Nk = p.Nk;
 
+    const int hk = h / p.group;           // key/value head of this query head
     const __bf16* qbase = (const __bf16*)p.q + (long long)b * p.q_sb + (long long)h * p.q_sh;
-    const char* kbase = (const char*)((const __bf16*)p.k + (long long)b * p.k_sb + (long long)h * p.k_sh);
-    const char* vbase = (const char*)((const __bf16*)p.v + (long long)b * p.k_sb + (long long)h * p.k_sh);
+    const char* kbase = (const char*)((const __bf16*)p.k + (long long)b * p.k_sb + (long long)hk * p.k_sh);
+    const char* vbase = (const char*)((const __bf16*)p.v + (long long)b * p.k_sb + (long long)hk * p.k_sh);
     const long long row_bytes = p.k_sn * 2;
 
-    // Key tiles this workgroup needs.  Tiles [0, n_full) need no mask for any
-    // wave (every key < Nk and, causal, <= the workgroup's first query); the
-    // rest are masked, and a wave skips the tiles past its last query
-    // (causal) or all of them if its rows are all padding.
+    // Key tiles this workgroup needs: [t_begin, n_kt).  Tiles [t_full_lo,
+    // n_full) need no mask for any wave (every key < Nk and, causal, <= the
+    // workgroup's first query; band: inside every row's band); the rest are
+    // masked, and a wave skips the tiles past its last visible key (causal,
+    // band) or all of them if its rows are all padding.
     int kv_end = Nk;
     if (CAUSAL) kv_end = min(Nk, min(q_wg0 + BR, Nq));
-    const int n_kt = (kv_end + BC - 1) / BC;
+    int n_kt = (kv_end + BC - 1) / BC;
     int n_full = Nk / BC;
     if (CAUSAL) n_full = min(n_full, (q_wg0 + 1) / BC);
     n_full = min(n_full, n_kt);
     // (padding waves, q_w0 >= Nq, run like the others: their Q rows are zero
     // and their results are not stored)
-    const int n_kt_wave = CAUSAL ? min(n_kt, (q_w0 + 31) / BC + 1) : n_kt;
+    int n_kt_wave = CAUSAL ? min(n_kt, (q_w0 + 31) / BC + 1) : n_kt;
+    int t_begin = 0, t_full_lo = 0;
+    // band limits of this lane's query (visible keys lo_key .. hi_key)
+    int lo_key = 0, hi_key = 0;
+    if constexpr (BAND) {
+        const int big = 1 << 30;
+        const int q_last = min(q_wg0 + BR, Nq) - 1;
+        const int wl = p.wl, wr = p.wr;
+        int key_lo = wl >= 0 ? max(0, q_wg0 - wl) : 0;          // first key any row sees
+        int key_hi = min(Nk - 1, wr >= 0 ? q_last + wr : big);  // last key any row sees
+        if (CAUSAL) key_hi = min(key_hi, q_last);
+        // tiles every row of the workgroup sees whole
+        int x_hi = min(Nk - 1, wr >= 0 ? q_wg0 + wr : big);
+        if (CAUSAL) x_hi = min(x_hi, q_wg0);
+        const int full_lo = wl >= 0 ? max(0, (q_last - wl + BC - 1) / BC) : 0;
+        if (key_lo > key_hi) {
+            t_begin = n_kt = n_full = t_full_lo = 0;           // no row sees any key
+        } else {
+            t_begin = key_lo / BC;
+            n_kt = key_hi / BC + 1;
+            t_full_lo = min(n_kt, max(t_begin, full_lo));
+            n_full = max(t_full_lo, min(n_kt, (x_hi + 1) / BC));
+        }
+        int w_hi = min(Nk - 1, wr >= 0 ? q_w0 + 31 + wr : big);
+        if (CAUSAL) w_hi = min(w_hi, q_w0 + 31);
+        n_kt_wave = min(n_kt, w_hi / BC + 1);
+        lo_key = wl >= 0 ? q - wl : -big;
+        hi_key = min(Nk - 1, wr >= 0 ? q + wr : big);
+        if (CAUSAL) hi_key = min(hi_key, q);
+    }
 
     // ---- Q fragment (B operand of S^T = K Q^T): lane holds Q[q][16kk + 8hi .. +7]
     bf16x8 qreg[KK];
@@ -358,12 +428,13 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     const unsigned long long vaddr = to_sgpr((unsigned long long)vbase);
     const unsigned long long tile_bytes = (unsigned long long)BC * (unsigned long long)row_bytes;
     lds_char* const ldst = lds + wave * 1024;   // this wave's rows of load round 0 in a stage
-#define FA_K_STAGE(t) (lds + ((t) & 1) * TB)
-#define FA_V_STAGE(t) (lds + (2 + ((t) & 1)) * TB)
+    // tile t lives in stage (t - t_begin) % 2 (t_begin = 0 without a band)
+#define FA_K_STAGE(t) (lds + (((t) - t_begin) & 1) * TB)
+#define FA_V_STAGE(t) (lds + (2 + (((t) - t_begin) & 1)) * TB)
 #define FA_ISSUE_K(t) issue_tile<LPW, DCH, BC, NW>(kaddr + (unsigned long long)(t) * tile_bytes, rb, ld_koff, \
-                                              ldst + ((t) & 1) * TB, Nk - (t) * BC, wave, lane)
+                                              ldst + (((t) - t_begin) & 1) * TB, Nk - (t) * BC, wave, lane)
 #define FA_ISSUE_V(t) issue_tile<LPW, DCH, BC, NW>(vaddr + (unsigned long long)(t) * tile_bytes, rb, ld_voff, \
-                                              ldst + (2 + ((t) & 1)) * TB, Nk - (t) * BC, wave, lane)
+                                              ldst + (2 + (((t) - t_begin) & 1)) * TB, Nk - (t) * BC, wave, lane)
 
     RowState<D> st;
 #pragma unroll
@@ -387,18 +458,24 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // every wave is done with step j-1) first refills the stages step j-1
     // read: K tile j+2 and V tile j+1; then computes P_j, O += P_j V_j and
     // the scores of tile j+1.
-    FA_ISSUE_K(0);
-    FA_ISSUE_V(0);
-    if (n_kt > 1) FA_ISSUE_K(1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    // Scores of tile 0.  Every row (padding rows included: their Q is zero)
-    // sees key 0, so the first max is finite.
     f32x16 sa[2], sb[2];   // scores of the current / next tile (roles alternate)
-    qk_tile<D>(sa, qreg, (const u32x4*)FA_K_STAGE(0), col, hi);
-    if (n_full == 0) mask_tile<CAUSAL>(sa, 0, q, Nk, hi);
-    st.m = tile_max_scaled(sa, sl2);
+    if (!BAND || n_kt > 0) {
+        FA_ISSUE_K(t_begin);
+        FA_ISSUE_V(t_begin);
+        if (t_begin + 1 < n_kt) FA_ISSUE_K(t_begin + 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+
+        // Scores of the first tile.  Without a band every row (padding rows
+        // included: their Q is zero) sees key 0, so the first max is finite.
+        qk_tile<D>(sa, qreg, (const u32x4*)FA_K_STAGE(t_begin), col, hi);
+        if constexpr (BAND) {
+            if (t_begin < t_full_lo || t_begin >= n_full) mask_tile_band(sa, t_begin * BC, lo_key, hi_key, hi);
+        } else {
+            if (n_full == 0) mask_tile<CAUSAL>(sa, 0, q, Nk, hi);
+        }
+        st.m = tile_max_scaled(sa, sl2);
+    }
 
 #define FA_TOP(j)                                      \
     do {                                               \
@@ -409,9 +486,25 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     } while (0)
 #define FA_KS(t) ((const u32x4*)FA_K_STAGE(t))
 
+    int j = t_begin;
+    if constexpr (BAND) {
+        // Masked first tiles (the band's left edge), serial, until the next
+        // tile is a whole one; then one more serial step if needed so the
+        // pipelined loop starts on stage 0.
+        for (; j + 1 < t_full_lo; ++j) {
+            FA_TOP(j);
+            wave_step_band<D, true>(st, sa, qreg, FA_KS(j + 1), FA_V_STAGE(j), (j + 1) * BC, lo_key, hi_key, sl2,
+                                    col, hi, tr_row, tr_dd);
+        }
+        if (((j - t_begin) & 1) && j + 1 < n_full) {
+            FA_TOP(j);
+            wave_step_band<D, true>(st, sa, qreg, FA_KS(j + 1), FA_V_STAGE(j), (j + 1) * BC, lo_key, hi_key, sl2,
+                                    col, hi, tr_row, tr_dd);
+            ++j;
+        }
+    }
     // Steps whose tiles j and j+1 are both unmasked, two at a time so the
     // score buffers swap roles without copies.
-    int j = 0;
     for (; j + 2 < n_full; j += 2) {
         FA_TOP(j);
         wave_step<D, CAUSAL, false, true>(st, sa, sb, qreg, FA_KS(j + 1), FA_V_STAGE(j), (j + 1) * BC, q, Nk,
@@ -425,12 +518,21 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     for (; j < n_kt; ++j) {
         FA_TOP(j);
         if (j < n_kt_wave) {
-            if (j + 1 < n_kt_wave)
-                wave_step_serial<D, CAUSAL, true>(st, sa, qreg, FA_KS(j + 1), FA_V_STAGE(j), (j + 1) * BC, q, Nk,
-                                                  sl2, col, hi, tr_row, tr_dd);
-            else
-                wave_step_serial<D, CAUSAL, false>(st, sa, qreg, nullptr, FA_V_STAGE(j), 0, q, Nk, sl2, col, hi,
-                                                   tr_row, tr_dd);
+            if constexpr (BAND) {
+                if (j + 1 < n_kt_wave)
+                    wave_step_band<D, true>(st, sa, qreg, FA_KS(j + 1), FA_V_STAGE(j), (j + 1) * BC, lo_key, hi_key,
+                                            sl2, col, hi, tr_row, tr_dd);
+                else
+                    wave_step_band<D, false>(st, sa, qreg, nullptr, FA_V_STAGE(j), 0, lo_key, hi_key, sl2, col, hi,
+                                             tr_row, tr_dd);
+            } else {
+                if (j + 1 < n_kt_wave)
+                    wave_step_serial<D, CAUSAL, true>(st, sa, qreg, FA_KS(j + 1), FA_V_STAGE(j), (j + 1) * BC, q, Nk,
+                                                      sl2, col, hi, tr_row, tr_dd);
+                else
+                    wave_step_serial<D, CAUSAL, false>(st, sa, qreg, nullptr, FA_V_STAGE(j), 0, q, Nk, sl2, col, hi,
+                                                       tr_row, tr_dd);
+            }
         }
     }
 
@@ -446,7 +548,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // the lane's half, recomputed (mbcnt) rather than kept live through the loops
     const int hi_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5;
     if (q < Nq) {
-        const float inv = 1.0f / l_tot;
+        // (band: a row that saw no key has l = 0 and gets O = 0, LSE = -inf)
+        const float inv = (!BAND || l_tot > 0.f) ? 1.0f / l_tot : 0.f;
         char* obase = (char*)p.o;
         const long long orow = (long long)b * p.q_sb + (long long)h * p.q_sh + (long long)q * p.q_sn;
 #pragma unroll
@@ -464,7 +567,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
                 }
             }
         if (p.lse && hi_e == 0)
-            p.lse[(long long)bh * Nq + q] = (st.m + __builtin_amdgcn_logf(l_tot)) * kLn2;
+            p.lse[(long long)bh * Nq + q] = (!BAND || l_tot > 0.f) ? (st.m + __builtin_amdgcn_logf(l_tot)) * kLn2
+                                                                   : -INFINITY;
     }
 }
 
@@ -621,9 +725,13 @@ constexpr int kWavesBf16 = FA_WAVES_BF16;   // queries per workgroup = 32 * wave
 constexpr int kWavesF32 = 4;
 
 template <int D, bool CAUSAL, bool OUT_BF16>
-hipError_t launch_bf16(const FwdParams& p, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, kWavesBf16, CAUSAL, OUT_BF16>), dim3(grid),
-                       dim3(kWavesBf16 * 64), 0, s, p);
+hipError_t launch_bf16(const FwdParams& p, int grid, bool band, hipStream_t s) {
+    if (band)
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, kWavesBf16, CAUSAL, OUT_BF16, true>), dim3(grid),
+                           dim3(kWavesBf16 * 64), 0, s, p);
+    else
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, kWavesBf16, CAUSAL, OUT_BF16, false>), dim3(grid),
+                           dim3(kWavesBf16 * 64), 0, s, p);
     return hipGetLastError();
 }
 
@@ -649,12 +757,14 @@ extern "C" const char* fa_status_str(int status) {
     }
 }
 
-extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                            int B, int H, int Nq, int Nk, int d, float scale, int causal,
-                            int layout, int in_dtype, int o_dtype, void* stream) {
+extern "C" fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                               int window_left, int window_right, int layout, int in_dtype, int o_dtype,
+                               void* stream) {
     // ---- validation: no HIP call before it passes
     if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
-    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
     if (layout != FA_BHND && layout != FA_BSND) return FA_ERR_INVALID_ARG;
     if (in_dtype != FA_BF16 && in_dtype != FA_F32) return FA_ERR_INVALID_ARG;
     if (o_dtype != FA_BF16 && o_dtype != FA_F32) return FA_ERR_INVALID_ARG;
@@ -663,6 +773,9 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     if (scale != scale || fabsf(scale) == INFINITY) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (in_dtype == FA_F32 && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+    const bool band = window_left >= 0 || window_right >= 0;
+    // the fp32 kernel serves plain attention only
+    if (in_dtype == FA_F32 && (band || Hkv != H)) return FA_ERR_UNSUPPORTED;
 
     const int rows_per_wg = 32 * (in_dtype == FA_BF16 ? kWavesBf16 : kWavesF32);
     const long long n_qtiles = ((long long)Nq + rows_per_wg - 1) / rows_per_wg;
@@ -670,7 +783,7 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     if ((long long)B * H > INT32_MAX || grid > INT32_MAX) return FA_ERR_UNSUPPORTED;
     // the bf16 kernel addresses a 64-row key tile with 32-bit byte offsets
     // (and row offsets with 24-bit multiplies)
-    const long long kv_row_bytes = (layout == FA_BSND ? (long long)H * d : (long long)d) * 2;
+    const long long kv_row_bytes = (layout == FA_BSND ? (long long)Hkv * d : (long long)d) * 2;
     if (in_dtype == FA_BF16 && 64 * kv_row_bytes >= (1LL << 30)) return FA_ERR_UNSUPPORTED;
 
     if (scale < 0.f) scale = 1.0f / sqrtf((float)d);
@@ -680,14 +793,17 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     const long long D = d;
     if (layout == FA_BHND) {
         p.q_sb = (long long)H * Nq * D; p.q_sh = (long long)Nq * D; p.q_sn = D;
-        p.k_sb = (long long)H * Nk * D; p.k_sh = (long long)Nk * D; p.k_sn = D;
+        p.k_sb = (long long)Hkv * Nk * D; p.k_sh = (long long)Nk * D; p.k_sn = D;
     } else {
         p.q_sb = (long long)Nq * H * D; p.q_sh = D; p.q_sn = (long long)H * D;
-        p.k_sb = (long long)Nk * H * D; p.k_sh = D; p.k_sn = (long long)H * D;
+        p.k_sb = (long long)Nk * Hkv * D; p.k_sh = D; p.k_sn = (long long)Hkv * D;
     }
     p.H = H; p.Nq = Nq; p.Nk = Nk;
     p.n_qtiles = (int)n_qtiles;
     p.BH = B * H;
+    p.group = H / Hkv;
+    p.wl = window_left < 0 ? -1 : window_left;
+    p.wr = window_right < 0 ? -1 : window_right;
     // scale 0 (uniform weights) runs as a tiny positive scale: every scaled
     // score is then below 2^-24 in magnitude and every probability rounds to
     // exactly 1, as with scale 0, while masked (-inf) scores still give 0.
@@ -698,16 +814,24 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     hipError_t err;
     if (in_dtype == FA_BF16) {
         const bool ob = o_dtype == FA_BF16;
+        const int g = (int)grid;
         if (d == 128) {
-            err = c ? (ob ? launch_bf16<128, true, true>(p, (int)grid, s) : launch_bf16<128, true, false>(p, (int)grid, s))
-                    : (ob ? launch_bf16<128, false, true>(p, (int)grid, s) : launch_bf16<128, false, false>(p, (int)grid, s));
+            err = c ? (ob ? launch_bf16<128, true, true>(p, g, band, s) : launch_bf16<128, true, false>(p, g, band, s))
+                    : (ob ? launch_bf16<128, false, true>(p, g, band, s) : launch_bf16<128, false, false>(p, g, band, s));
         } else {
-            err = c ? (ob ? launch_bf16<64, true, true>(p, (int)grid, s) : launch_bf16<64, true, false>(p, (int)grid, s))
-                    : (ob ? launch_bf16<64, false, true>(p, (int)grid, s) : launch_bf16<64, false, false>(p, (int)grid, s));
+            err = c ? (ob ? launch_bf16<64, true, true>(p, g, band, s) : launch_bf16<64, true, false>(p, g, band, s))
+                    : (ob ? launch_bf16<64, false, true>(p, g, band, s) : launch_bf16<64, false, false>(p, g, band, s));
         }
     } else {
         if (d == 128) err = c ? launch_f32<128, true>(p, (int)grid, s) : launch_f32<128, false>(p, (int)grid, s);
         else err = c ? launch_f32<64, true>(p, (int)grid, s) : launch_f32<64, false>(p, (int)grid, s);
     }
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                            int layout, int in_dtype, int o_dtype, void* stream) {
+    return fa_fwd_ex(q, k, v, o, lse, B, H, H, Nq, Nk, d, scale, causal, -1, -1, layout, in_dtype, o_dtype,
+                     stream);
 }

@@ -51,6 +51,25 @@ class Workload:
     sigma_v: float = 1.0
     peaked_frac: float = 0.0   # fraction of K rows scaled by peaked_mult
     peaked_mult: float = 8.0
+    Hkv: int = 0               # key/value heads (0: H); query head h reads KV head h // (H // Hkv)
+    window: tuple = (-1, -1)   # band (left, right): keys i-left .. i+right visible; negative: unbounded
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
+
+    @property
+    def visible_pairs(self) -> int:
+        """Visible (query, key) pairs of one head under the causal flag and the band."""
+        lo_w, hi_w = self.window
+        total = 0
+        for i in range(self.Nq):
+            lo = max(0, i - lo_w) if lo_w >= 0 else 0
+            hi = min(self.Nk - 1, i + hi_w) if hi_w >= 0 else self.Nk - 1
+            if self.causal:
+                hi = min(hi, i)
+            total += max(0, hi - lo + 1)
+        return total
 
     @property
     def scale(self) -> float:
@@ -58,7 +77,10 @@ class Workload:
 
     @property
     def flops(self) -> float:
-        """4*B*H*Nq*Nk*d, halved for causal (the dense count, not N(N+1)/2)."""
+        """4*B*H*Nq*Nk*d, halved for causal (the dense count, not N(N+1)/2);
+        with a band, 4*B*H*d per visible (query, key) pair."""
+        if self.window != (-1, -1):
+            return 4.0 * self.B * self.H * self.d * self.visible_pairs
         f = 4.0 * self.B * self.H * self.Nq * self.Nk * self.d
         return f / 2 if self.causal else f
 
@@ -66,12 +88,13 @@ class Workload:
         return self._shape(self.Nq)
 
     def kv_shape(self):
-        return self._shape(self.Nk)
+        return self._shape(self.Nk, self.kv_heads)
 
-    def _shape(self, n):
+    def _shape(self, n, heads=None):
+        heads = self.H if heads is None else heads
         if self.layout == "BHND":
-            return (self.B, self.H, n, self.d)
-        return (self.B, n, self.H, self.d)
+            return (self.B, heads, n, self.d)
+        return (self.B, n, heads, self.d)
 
     def scaled(self, **changes) -> "Workload":
         return dataclasses.replace(self, **changes)
@@ -87,6 +110,11 @@ WORKLOADS = {
                              sigma_k=0.5, sigma_v=0.5),
     "long_causal_128k": Workload(5, "long_causal_128k", 1, 32, 131072, 131072, 128,
                                  "bf16", "BSND", True, peaked_frac=0.01),
+    # the inference-side variants of the pages' next rows: grouped KV heads
+    # ([nanhubrain] "GatherPAKVCache", GQA/MQA) under a causal sliding window
+    # ([pwwt] pre_tokens / next_tokens), at the LLaMA-like 32 x 128 head shape
+    "gqa_swa_prefill": Workload(6, "gqa_swa_prefill", 1, 32, 16384, 16384, 128, "bf16", "BSND", True,
+                                Hkv=8, window=(4095, -1)),
 }
 BY_ID = {w.cid: w for w in WORKLOADS.values()}
 
@@ -150,9 +178,9 @@ def peaked_positions(w: Workload, seed_base: int | None = None) -> np.ndarray | 
     base = 1000 * w.cid if seed_base is None else seed_base
     n = int(round(w.peaked_frac * w.Nk))
     g = np.random.Generator(np.random.PCG64(base + 3))
-    pos = np.empty((w.B, w.H, n), dtype=np.int64)
+    pos = np.empty((w.B, w.kv_heads, n), dtype=np.int64)
     for b in range(w.B):
-        for h in range(w.H):
+        for h in range(w.kv_heads):
             pos[b, h] = np.sort(g.choice(w.Nk, size=n, replace=False))
     return pos
 
@@ -168,7 +196,7 @@ def make_inputs(w: Workload, seed_base: int | None = None) -> Inputs:
     if pos is not None:
         mult = np.float32(w.peaked_mult)
         for b in range(w.B):
-            for h in range(w.H):
+            for h in range(w.kv_heads):
                 if w.layout == "BHND":
                     k[b, h, pos[b, h], :] *= mult
                 else:

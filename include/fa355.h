@@ -90,6 +90,32 @@ FA355_API fa_status fa_fwd(const void* q, const void* k, const void* v, void* o,
                            int layout, int in_dtype, int o_dtype, void* stream);
 
 /*
+ * fa_fwd_ex -- fa_fwd with grouped key/value heads and a band of visible keys.
+ *
+ * Hkv      number of key/value heads, >= 1, dividing H: query head h reads
+ *          key/value head h / (H / Hkv) (grouped-query attention; Hkv = 1 is
+ *          multi-query, Hkv = H plain).  k and v have Hkv heads in `layout`
+ *          ([B,Hkv,Nk,d] or [B,Nk,Hkv,d]).  Only the needed heads are read
+ *          ([nanhubrain] "GatherPAKVCache": head selection for GQA/MQA).
+ * window_left, window_right
+ *          the band of [pwwt] "standard vs IO-aware" (pre_tokens /
+ *          next_tokens): key j is visible to query i iff
+ *          i - window_left <= j <= i + window_right; a negative value leaves
+ *          that side unbounded.  `causal` still applies (j <= i) on top; a
+ *          causal sliding window is (w, -1) with causal = 1, or (w, 0).
+ *          Key tiles outside a query tile's band are never loaded.  A row
+ *          with no visible key gets O = 0 and LSE = -inf.
+ * All other arguments, the alignment, ownership and asynchrony rules are
+ * those of fa_fwd; fa_fwd(...) is fa_fwd_ex(..., Hkv = H, window -1, -1).
+ * FA_ERR_INVALID_ARG also when H % Hkv != 0; FA_ERR_UNSUPPORTED for fp32
+ * inputs with Hkv != H or a band.
+ */
+FA355_API fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                              int window_left, int window_right, int layout, int in_dtype, int o_dtype,
+                              void* stream);
+
+/*
  * fa_bwd -- enqueue the attention backward pass on `stream`: the gradients of
  * a loss L with respect to Q, K and V, given dO = dL/dO.
  *

@@ -161,3 +161,29 @@ def test_bwd_python_wrapper_validates_without_gpu():
     l = torch.zeros(1, 1, 4)
     with pytest.raises(ValueError):
         fa.bwd(x, x, x, x, x, l)               # CPU tensors are refused
+
+
+XGOOD = dict(GOOD, Hkv=2, wl=-1, wr=-1)
+
+
+def xcall(**changes):
+    a = dict(XGOOD, **changes)
+    return fa.fa_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"],
+                        a["d"], a["scale"], a["causal"], a["wl"], a["wr"], a["layout"], a["in_dtype"],
+                        a["o_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("changes,status", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=3, Hkv=2), fa.FA_ERR_INVALID_ARG),      # H not a multiple of Hkv
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(layout=3), fa.FA_ERR_INVALID_ARG),
+    (dict(v=P + 0x2004), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=math.nan), fa.FA_ERR_INVALID_ARG),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(in_dtype=fa.FA_F32, H=2, Hkv=1), fa.FA_ERR_UNSUPPORTED),   # fp32: plain attention only
+    (dict(in_dtype=fa.FA_F32, wl=4), fa.FA_ERR_UNSUPPORTED),
+])
+def test_fwd_ex_validation_returns_before_launch(changes, status):
+    assert xcall(**changes) == status
