@@ -222,6 +222,81 @@ def make_grad(w: Workload, seed_base: int | None = None):
     return g, None
 
 
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """Decode attention over a paged KV cache: Nq new tokens per sequence
+    attend to the sequence's L_b cached keys (the tokens sit at positions
+    L_b - Nq .. L_b - 1; causal: token t sees keys j <= L_b - Nq + t)."""
+    cid: int
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    Nq: int                 # new tokens per sequence
+    max_len: int            # longest sequence (keys)
+    min_len: int            # shortest sequence
+    d: int
+    block_size: int         # tokens per KV cache block
+    causal: bool = False
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def max_blocks(self) -> int:
+        return (self.max_len + self.block_size - 1) // self.block_size
+
+    def scaled(self, **changes) -> "DecodeWorkload":
+        return dataclasses.replace(self, **changes)
+
+
+DECODE_WORKLOADS = {
+    # one new token per sequence for a batch of 32 LLaMA-like (32 x 128) heads
+    # with 8 KV heads, 4K-8K tokens cached in blocks of 16 ([nanhubrain]
+    # "GatherPAKVCache": paged cache, block tables, GQA head selection)
+    "decode_paged_gqa": DecodeWorkload(7, "decode_paged_gqa", 32, 32, 8, 1, 8192, 4096, 128, 16),
+}
+
+
+@dataclasses.dataclass
+class PagedInputs:
+    w: DecodeWorkload
+    q: np.ndarray            # [B, Nq, H, d] float32 values
+    k_cache: np.ndarray      # [num_blocks, block_size, Hkv, d] float32 values
+    v_cache: np.ndarray
+    q_bits: np.ndarray       # bf16 bits of the same
+    k_bits: np.ndarray
+    v_bits: np.ndarray
+    seq_lens: np.ndarray     # [B] int32
+    block_tables: np.ndarray  # [B, max_blocks] int32 physical block ids (-1: unused)
+
+
+def make_paged(w: DecodeWorkload, seed_base: int | None = None) -> PagedInputs:
+    """Seeded paged-cache inputs: sequence lengths uniform in [min_len,
+    max_len] (seed +5); every sequence's blocks are distinct physical blocks
+    of one cache, in a seeded random order (seed +6), with one spare block at
+    the end of the cache that no table references; Q, K cache, V cache
+    N(0, 1) (seeds +0, +1, +2), rounded to bf16."""
+    base = 1000 * w.cid if seed_base is None else seed_base
+    g = np.random.Generator(np.random.PCG64(base + 5))
+    lens = g.integers(w.min_len, w.max_len + 1, size=w.B).astype(np.int32)
+    nblk = (lens + w.block_size - 1) // w.block_size
+    total = int(nblk.sum()) + 1
+    perm = np.random.Generator(np.random.PCG64(base + 6)).permutation(total - 1).astype(np.int32)
+    tables = np.full((w.B, w.max_blocks), -1, dtype=np.int32)
+    at = 0
+    for b in range(w.B):
+        tables[b, :nblk[b]] = perm[at:at + nblk[b]]
+        at += nblk[b]
+    q = _draw(base + 0, (w.B, w.Nq, w.H, w.d), 1.0)
+    kc = _draw(base + 1, (total, w.block_size, w.Hkv, w.d), 1.0)
+    vc = _draw(base + 2, (total, w.block_size, w.Hkv, w.d), 1.0)
+    qb, kb, vb = f32_to_bf16_bits(q), f32_to_bf16_bits(kc), f32_to_bf16_bits(vc)
+    return PagedInputs(w, bf16_bits_to_f32(qb), bf16_bits_to_f32(kb), bf16_bits_to_f32(vb), qb, kb, vb,
+                       lens, tables)
+
+
 def sample_rows(w: Workload, n: int, seed: int = 7, peaked: np.ndarray | None = None) -> np.ndarray:
     """A sorted, de-duplicated sample of query rows for row-sampled checks:
     the first 16 and last 16 rows, up to 16 rows right after peaked keys of

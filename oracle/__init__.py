@@ -28,6 +28,11 @@ Four implementations live here:
   with the online-softmax recurrence ([nanhubrain] "tiling skeleton",
   [ascendai] section 2.2), in numpy fp64, over caller-chosen block splits.
 
+``paged.gather_paged_kv`` / ``paged.decode_reference`` (numpy) gather a
+paged KV cache the way [nanhubrain] "GatherPAKVCache" describes (logical block
+-> physical block through the block table, optional KV head selection) and
+run ``attn_fwd_ex`` on the gathered sequence for decode attention.
+
 Page key: [nanhubrain] = nanhubrain.csdn.net (FlashAttention in CANN
 ops-transformer), [pwwt] = www.pwwt.cn/news/2518640, [ascendai] =
 ascendai.csdn.net (efficient attention in CANN ops-nn).
