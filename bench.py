@@ -59,7 +59,7 @@ def algorithmic_bytes(w, out_bytes: int) -> float:
 # the kernels' sources (their file and the shared device header)
 KERNEL_SOURCES = {
     p: [os.path.join(ROOT, "exact_attention_112_amd", "csrc", n) for n in (f"fa_{p}.hip", "fa_common.h")]
-    for p in ("fwd", "bwd")
+    for p in ("fwd", "bwd", "decode")
 }
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -180,6 +180,106 @@ def cpu_baseline_bwd(w, inp, grad, target_s: float = 10.0):
     }
 
 
+def decode_bytes(w, lens) -> float:
+    """Algorithmic bytes of one decode call: every cached K and V row of every
+    sequence read once (bf16), Q read and O (fp32) and LSE written once, the
+    block tables and lengths read once."""
+    kv = 2.0 * float(sum(int(x) for x in lens)) * w.Hkv * w.d * 2
+    qo = w.B * w.Nq * w.H * w.d * (2 + 4) + w.B * w.H * w.Nq * 4
+    return kv + qo + w.B * w.max_blocks * 4 + w.B * 4
+
+
+def cpu_baseline_decode(w, inp, target_s: float = 10.0):
+    """Time the decode oracle (block-table gather + fp64 forward) sequence by
+    sequence until ``target_s`` seconds are done; rate in GB/s of the
+    algorithmic bytes of the sequences covered."""
+    import oracle
+    from oracle import paged
+
+    lib = oracle.lib()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or lib.max_threads()
+    done, elapsed, nbytes = 0, 0.0, 0.0
+    while done < w.B and elapsed < target_s:
+        b = done
+        t0 = time.perf_counter()
+        paged.decode_reference(lib, inp.q[b:b + 1], inp.k_cache, inp.v_cache, inp.block_tables[b:b + 1],
+                               inp.seq_lens[b:b + 1], scale=w.scale, causal=w.causal)
+        elapsed += time.perf_counter() - t0
+        nbytes += decode_bytes(w.scaled(B=1), inp.seq_lens[b:b + 1])
+        done += 1
+    return {
+        "value": nbytes / elapsed / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"block-table gather + fp64 oracle on the first {done} of {w.B} sequences of {w.name}; "
+                   f"{nbytes:.3e} algorithmic bytes in {elapsed:.1f} s on {threads} threads"),
+    }
+
+
+def bench_decode(args, w):
+    """One step = one fa_decode call (split kernel + merge kernel)."""
+    import numpy as np
+    import torch
+    import exact_attention_112_amd as fa
+    from exact_attention_112_amd import inputs as I
+
+    print(f"bench: generating inputs for {w.name}", file=sys.stderr, flush=True)
+    inp = I.make_paged(w)
+    t = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda")
+    tq, kc, vc = t(inp.q_bits), t(inp.k_bits), t(inp.v_bits)
+    bt = torch.from_numpy(inp.block_tables).to("cuda")
+    sl = torch.from_numpy(inp.seq_lens).to("cuda")
+    need = fa.fa_decode_workspace_bytes(w.B, w.H, w.Hkv, w.Nq, w.d, w.max_blocks * w.block_size)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o = torch.empty(tq.shape, dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+
+    def step():
+        fa.decode(tq, kc, vc, bt, sl, causal=w.causal, scale=w.scale, workspace=ws, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    if not torch.isfinite(o).all():
+        print("bench: non-finite output", file=sys.stderr)
+        return 1
+    nbytes = decode_bytes(w, inp.seq_lens)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    cpu = None if args.no_cpu_baseline else cpu_baseline_decode(w, inp)
+    line = {
+        "metric": f"attention decode GB/s and % of HBM peak at {w.name}",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q and paged K/V cache, seeded lengths and block placement)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "Nq": w.Nq, "max_len": w.max_len,
+                   "min_len": w.min_len, "d": w.d, "block_size": w.block_size, "causal": w.causal,
+                   "pass": "decode"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_from_profiles(w.name, "decode")},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,8 +318,10 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n * 4}), flush=True)
         return 0
-    w = I.WORKLOADS[args.workload]
     fa.load()
+    if args.workload in I.DECODE_WORKLOADS:
+        return bench_decode(args, I.DECODE_WORKLOADS[args.workload])
+    w = I.WORKLOADS[args.workload]
     print(f"bench: generating inputs for {w.name}", file=sys.stderr, flush=True)
     inp = I.make_inputs(w)
     if w.dtype == "bf16":

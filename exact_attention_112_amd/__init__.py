@@ -34,7 +34,8 @@ FA_BF16, FA_F32 = 0, 1
 LAYOUTS = {"BHND": FA_BHND, "BSND": FA_BSND}
 
 # the symbols include/fa355.h declares
-EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_status_str", "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_decode", "fa_decode_workspace_bytes", "fa_status_str",
+           "fa_abi_version")
 ABI_VERSION = 1
 
 _lib = None
@@ -72,6 +73,11 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.fa_fwd_ex.restype = ctypes.c_int
     lib.fa_fwd_ex.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [ctypes.c_float]
                               + [ctypes.c_int] * 6 + [ctypes.c_void_p])
+    lib.fa_decode.restype = ctypes.c_int
+    lib.fa_decode.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.c_size_t] + [ctypes.c_int] * 7 + [ctypes.c_float]
+                              + [ctypes.c_int] * 3 + [ctypes.c_void_p])
+    lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_decode_workspace_bytes.argtypes = [ctypes.c_int] * 6
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float]
                            + [ctypes.c_int] * 4 + [ctypes.c_void_p])
@@ -245,3 +251,74 @@ def bwd(q, k, v, o, do, lse, *, causal: bool = False, scale: float | None = None
     if st != FA_OK:
         raise FaError(st, "HIP launch failed")
     return dq, dk, dv
+
+
+def fa_decode(q: int, k_cache: int, v_cache: int, block_tables: int, seq_lens: int, o: int, lse: int | None,
+              workspace: int, workspace_bytes: int, B: int, H: int, Hkv: int, Nq: int, d: int, block_size: int,
+              max_blocks: int, scale: float, causal: int, in_dtype: int, o_dtype: int,
+              stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the fa_status."""
+    return int(load().fa_decode(q, k_cache, v_cache, block_tables, seq_lens, o, lse or None, workspace,
+                                int(workspace_bytes), B, H, Hkv, Nq, d, block_size, max_blocks, float(scale),
+                                int(causal), int(in_dtype), int(o_dtype), stream or None))
+
+
+def fa_decode_workspace_bytes(B: int, H: int, Hkv: int, Nq: int, d: int, max_seq_len: int) -> int:
+    return int(load().fa_decode_workspace_bytes(B, H, Hkv, Nq, d, max_seq_len))
+
+
+def decode(q, k_cache, v_cache, block_tables, seq_lens, *, causal: bool = False, scale: float | None = None,
+           out_dtype=None, workspace=None, return_lse: bool = True, out=None, lse=None):
+    """Decode attention over a paged KV cache on torch CUDA tensors (ROCm).
+
+    q: [B, Nq, H, d] bf16; k_cache, v_cache: [num_blocks, block_size, Hkv, d]
+    bf16; block_tables: int32 [B, max_blocks]; seq_lens: int32 [B].  Returns
+    (O [B, Nq, H, d] of ``out_dtype`` (default float32), LSE float32
+    [B, H, Nq]).  ``workspace``: optional uint8 device tensor of at least
+    fa_decode_workspace_bytes(...) bytes (allocated here when not given).
+    """
+    import torch
+
+    ts = (q, k_cache, v_cache, block_tables, seq_lens)
+    if any(not t.is_cuda for t in ts) or len({t.device for t in ts}) != 1:
+        raise ValueError("all tensors must be on one GPU")
+    if not all(t.is_contiguous() for t in ts):
+        raise ValueError("all tensors must be contiguous")
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise ValueError("q, k_cache, v_cache must be bfloat16")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_tables and seq_lens must be int32")
+    if q.dim() != 4 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B,Nq,H,d]; k_cache and v_cache the same [blocks,block_size,Hkv,d]")
+    B, Nq, H, d = q.shape
+    _, block_size, Hkv, dk = k_cache.shape
+    if dk != d or block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("shapes disagree")
+    max_blocks = block_tables.shape[1]
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    need = fa_decode_workspace_bytes(B, H, Hkv, Nq, d, max_blocks * block_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    o = torch.empty(q.shape, dtype=out_dtype, device=q.device) if out is None else out
+    if o.shape != q.shape or o.dtype != out_dtype or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("out must be a contiguous tensor of q's shape and out_dtype on q's device")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B,H,Nq] tensor")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                       seq_lens.data_ptr(), o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                       workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, H, Hkv, Nq, d,
+                       block_size, max_blocks, -1.0 if scale is None else float(scale), int(bool(causal)),
+                       FA_BF16, FA_BF16 if out_dtype == torch.bfloat16 else FA_F32, stream)
+    if st == FA_ERR_INVALID_ARG:
+        raise FaInvalidArgument(st, "invalid argument")
+    if st == FA_ERR_UNSUPPORTED:
+        raise FaUnsupported(st, "unsupported configuration")
+    if st != FA_OK:
+        raise FaError(st, "HIP launch failed")
+    return o, lse

@@ -7,7 +7,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "fa_fwd.hip"), os.path.join(PKG, "csrc", "fa_bwd.hip")]
+SOURCES = [os.path.join(PKG, "csrc", n) for n in ("fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libfa355.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

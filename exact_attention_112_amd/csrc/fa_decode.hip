@@ -1,0 +1,376 @@
+// fa_decode.hip -- decode attention over a paged KV cache, gfx950.
+//
+// Nq new tokens per sequence (token t of sequence b at position
+// L_b - Nq + t) attend to the sequence's L_b cached keys, which live in a
+// paged cache: [num_blocks, block_size, Hkv, d] for K and for V, with
+// logical block i of sequence b in physical block block_tables[b][i]
+// ([nanhubrain] "GatherPAKVCache": block tables, and only the KV heads the
+// grouped query heads need).  The page gathers the blocks into a contiguous
+// copy first; here the attention kernel reads the blocks in place, so the
+// cache is read from HBM exactly once and nothing is copied.
+//
+// The keys of a sequence are split into S chunks (split-KV); each (sequence,
+// KV head, row tile, chunk) is one wavefront that runs the online softmax
+// over its chunk and writes a partial (O_s normalised, LSE_s); a second
+// kernel merges the chunks with the online-softmax merge of [nanhubrain]
+// "online softmax mathematics" applied once per chunk:
+//   LSE = log sum_s exp(LSE_s),  O = sum_s exp(LSE_s - LSE) O_s.
+//
+// gfx950 design:
+//   * rows of a wave = the grouped query heads of one KV head times the new
+//     tokens (32 per row tile), the MFMA B operand, held in VGPRs;
+//   * a lane owns one key row of a 32-key tile: its K fragments come
+//     straight from the paged cache into the A operand registers of
+//     S^T = K Q^T (v_mfma_f32_32x32x16_bf16), one tile ahead; the same
+//     lane stages the same key row of V into LDS with global_load_lds_dwordx4
+//     (16 bytes a lane, per-lane 64-bit addresses), so one block-table
+//     lookup per lane and tile serves both;
+//   * the V tile is stored chunk-major (the 32 rows of each 16-byte d chunk
+//     contiguous), the order in which one lane's loads of one key row land;
+//     the transposing reads (ds_read_b64_tr_b16) of O^T += V^T P^T then meet
+//     2-way bank conflicts, far below the cache read time of a tile;
+//   * the four waves of a workgroup are independent (no barriers), 16 KB of
+//     LDS each (two V stages at d = 128).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "fa355.h"
+#include "fa_common.h"
+
+namespace fa355 {
+
+struct DecodeParams {
+    const void* q;            // [B, Nq, H, d] bf16
+    const void* k_cache;      // [num_blocks, block_size, Hkv, d] bf16
+    const void* v_cache;
+    const int* block_tables;  // [B, max_blocks]
+    const int* seq_lens;      // [B]
+    float* part_o;            // [B, H, Nq, S, d] fp32 partial outputs (normalised)
+    float* part_lse;          // [B, H, Nq, S] fp32 partial log-sum-exps
+    void* o;                  // [B, Nq, H, d]
+    float* lse;               // [B, H, Nq] or NULL
+    int B, H, Hkv, Nq;
+    int group;                // H / Hkv
+    int G;                    // rows per KV head: group * Nq
+    int n_rt;                 // row tiles of 32: ceil(G / 32)
+    int S;                    // key chunks per sequence
+    int chunk;                // keys per chunk (multiple of 32)
+    int bs_log2;              // log2(block_size)
+    int max_blocks;
+    float scale_log2;         // scale * log2(e) (tiny positive for scale 0)
+};
+
+// The V tile's LDS slot (16-byte units) of key row `row`, d chunk `c`.
+__device__ __forceinline__ int v_slot(int row, int c) { return c * 32 + row; }
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_decode_split_kernel(DecodeParams p) {
+    constexpr int NWV = 4, TK = 32, DCH = D / 8, KK = D / 16, DB = D / 32;
+    constexpr int STAGE = TK * DCH;          // 16-byte slots per V stage
+    constexpr int LPT = DCH / 2;             // V loads per lane per tile
+    __shared__ u32x4 smem[NWV * 2 * STAGE];
+
+    const int tid = __builtin_amdgcn_workitem_id_x();
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31;
+    const int hi = lane >> 5;
+
+    const int total = p.B * p.Hkv * p.n_rt * p.S;
+    const int item = __builtin_amdgcn_workgroup_id_x() * NWV + wave;
+    if (item >= total) return;                       // whole wave; no barriers below
+    int rest = item;
+    const int s = rest % p.S; rest /= p.S;
+    const int rt = rest % p.n_rt; rest /= p.n_rt;
+    const int hk = rest % p.Hkv;
+    const int b = rest / p.Hkv;
+
+    const int cap = p.max_blocks << p.bs_log2;
+    const int L = min(max(p.seq_lens[b], 0), cap);
+    const int k_begin = s * p.chunk;
+    const int k_end = min(L, k_begin + p.chunk);
+
+    // this lane's row (for the B operand and the outputs): row r of the
+    // KV head's rows, token t = r / group, query head hk*group + r % group
+    const int r = rt * 32 + col;
+    const bool row_ok = r < p.G;
+    const int t = row_ok ? r / p.group : 0;
+    const int h = hk * p.group + (row_ok ? r % p.group : 0);
+    // last key this row sees
+    const int hi_key = CAUSAL ? min(L - 1, L - p.Nq + t) : L - 1;
+
+    const long long q_row = (((long long)b * p.Nq + t) * p.H + h) * D;
+    bf16x8 qreg[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        const u32x4 x = row_ok ? *(const u32x4*)((const __bf16*)p.q + q_row + kk * 16 + hi * 8)
+                               : (u32x4){0u, 0u, 0u, 0u};
+        qreg[kk] = __builtin_bit_cast(bf16x8, x);
+    }
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+    float m = -INFINITY, l0 = 0.f, l1 = 0.f;
+    const float sl2 = p.scale_log2;
+
+    lds_char* const vst = (lds_char*)smem + wave * 2 * STAGE * 16;
+    const int* table = p.block_tables + (long long)b * p.max_blocks;
+    const long long head_off = (long long)hk * D;             // elements
+    const long long row_stride = (long long)p.Hkv * D;        // elements per token of a block
+
+    // byte address of key `key`'s row (this KV head) in a cache
+    auto key_row = [&](int key) -> long long {
+        const int kc = min(key, k_end - 1);                   // past the chunk: the last key (masked)
+        const int blk = table[kc >> p.bs_log2];
+        const long long tok = ((long long)blk << p.bs_log2) + (kc & ((1 << p.bs_log2) - 1));
+        return (tok * row_stride + head_off) * 2;
+    };
+    // tile i: K fragments of this lane's key row into kf; the same row of V
+    // into V stage (i & 1) (chunks 2j + hi, j < LPT)
+    auto load_tile = [&](int i, u32x4 (&kf)[KK]) {
+        const long long off = key_row(k_begin + i * TK + col);
+        const char* kr = (const char*)p.k_cache + off;
+        const char* vr = (const char*)p.v_cache + off;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kf[kk] = *(const u32x4*)(kr + (2 * kk + hi) * 16);
+        lds_char* stg = vst + (i & 1) * STAGE * 16;
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) {
+            // lane (col, hi) of load j writes slot j*64 + lane = (2j + hi)*32 + col:
+            // chunk c = 2j + hi of key row col
+            const int c = 2 * j + hi;
+            __builtin_amdgcn_global_load_lds((const void*)(vr + c * 16), (lds_void*)(stg + j * 1024), 16, 0, 0);
+        }
+    };
+
+    const int n_tiles = k_end > k_begin ? (k_end - k_begin + TK - 1) / TK : 0;
+    u32x4 kf[KK], kn[KK];
+    if (n_tiles > 0) load_tile(0, kf);
+
+    const int tg = lane >> 4, ti = lane & 15;
+    const int tr_row = hi * 4 + (ti >> 2);
+    const int tr_dd = 16 * (tg & 1) + 4 * (ti & 3);
+
+    for (int i = 0; i < n_tiles; ++i) {
+        // tile i's V is in LDS and its K fragments in kf once every load is back
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (i + 1 < n_tiles) {
+            // the stage tile i+1 refills was last read by tile i-1, finished
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            load_tile(i + 1, kn);
+        }
+        const int key0 = k_begin + i * TK;
+        f32x16 sc;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[kk]), qreg[kk],
+                                                         kk == 0 ? f32x16{} : sc, 0, 0, 0);
+        // keys past the chunk or (causal) after the row's token -> -inf
+        const int lim = min(k_end - 1, hi_key) - (key0 + hi * 4);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            sc[e] = ((e >> 2) * 8 + (e & 3)) <= lim ? sc[e] : -INFINITY;
+        float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+#pragma unroll
+        for (int e = 3; e < 15; e += 2) mx = fmaxf(fmaxf(mx, sc[e]), sc[e + 1]);
+        const float mt = pair_max(fmaxf(mx, sc[15])) * sl2;
+        if (mt > m) {                                   // per lane; alpha = 0 when m was -inf
+            const float alpha = __builtin_amdgcn_exp2f(m - mt);
+            l0 *= alpha;
+            l1 *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+            m = mt;
+        }
+        const float nm = -fmaxf(m, -3.0e38f);           // finite for rows with no key yet
+        unsigned pk[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * jj], sl2, nm));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * jj + 1], sl2, nm));
+            l0 += e0;
+            l1 += e1;
+            pk[jj] = pack_bf16x2(e0, e1);
+        }
+        // O^T += V^T P^T: slots 0..3 of 16-key group u are keys 16u + hi*4 + 0..3,
+        // slots 4..7 keys 16u + 8 + hi*4 + 0..3
+        const lds_char* stg = vst + (i & 1) * STAGE * 16;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, (u32x4){pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]});
+            const int r0 = 16 * u + tr_row, r1 = r0 + 8;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int dd = db * 32 + tr_dd;
+                const int c = dd >> 3, w = (dd & 7) * 2;
+                const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4*)(stg + v_slot(r0, c) * 16 + w));
+                const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4*)(stg + v_slot(r1, c) * 16 + w));
+                const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[db], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kf[kk] = kn[kk];
+    }
+
+    // partial result of this chunk: O_s = acc / l (0 if the row saw no key),
+    // LSE_s = m + log2(l) in natural-log units (-inf if no key)
+    const float l_tot = pair_sum(l0 + l1);
+    if (row_ok) {
+        const long long prow = (((long long)b * p.H + h) * p.Nq + t) * p.S + s;
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        float* po = p.part_o + prow * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int dd = db * 32 + g * 8 + hi * 4;
+                *(float4*)(po + dd) = make_float4(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
+                                                  oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+            }
+        if (hi == 0) p.part_lse[prow] = l_tot > 0.f ? (m + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    }
+}
+
+// Merge the S partial results of each (b, h, token) row: one wave per row.
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void fa_decode_merge_kernel(DecodeParams p) {
+    constexpr int EPL = D / 64;   // elements per lane
+    const int tid = __builtin_amdgcn_workitem_id_x();
+    const int lane = tid & 63;
+    const long long row = (long long)__builtin_amdgcn_workgroup_id_x() * 4 + (tid >> 6);
+    const long long n_rows = (long long)p.B * p.H * p.Nq;
+    if (row >= n_rows) return;
+    const int t = (int)(row % p.Nq);
+    const long long bh = row / p.Nq;
+    const int h = (int)(bh % p.H);
+    const int b = (int)(bh / p.H);
+    const float* pl = p.part_lse + row * p.S;
+    float mx = -INFINITY;
+    for (int s = 0; s < p.S; ++s) mx = fmaxf(mx, pl[s]);
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+    float z = 0.f;
+    if (mx > -INFINITY) {
+        for (int s = 0; s < p.S; ++s) {
+            const float w = __expf(pl[s] - mx);        // 0 for an empty chunk (-inf)
+            z += w;
+            const float* po = p.part_o + (row * p.S + s) * D + lane * EPL;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(w, po[e], acc[e]);
+        }
+    }
+    const float inv = z > 0.f ? 1.0f / z : 0.f;
+    const long long orow = (((long long)b * p.Nq + t) * p.H + h) * D + lane * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        const float v = acc[e] * inv;
+        if constexpr (OUT_BF16) ((__bf16*)p.o)[orow + e] = (__bf16)v;
+        else ((float*)p.o)[orow + e] = v;
+    }
+    if (p.lse && lane == 0) p.lse[bh * p.Nq + t] = z > 0.f ? mx + __logf(z) : -INFINITY;
+}
+
+}  // namespace fa355
+
+using namespace fa355;
+
+namespace {
+
+bool aligned_d(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
+
+// Key chunks per sequence: enough work items to give every CU's eight waves
+// one item (2048 on MI355X), no chunk shorter than 256 keys.
+int decode_splits(int B, int H, int Hkv, int Nq, int max_len) {
+    const long long G = (long long)(H / Hkv) * Nq;
+    const long long base = (long long)B * Hkv * ((G + 31) / 32);
+    long long S = (2048 + base - 1) / base;
+    const long long cap = (max_len + 255) / 256;
+    if (S > cap) S = cap;
+    if (S < 1) S = 1;
+    return (int)S;
+}
+
+}  // namespace
+
+extern "C" size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int Nq, int d, int max_seq_len) {
+    if (B < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 || Nq < 1 || d < 1 || max_seq_len < 1) return 0;
+    const long long S = decode_splits(B, H, Hkv, Nq, max_seq_len);
+    return (size_t)((long long)B * H * Nq * S * (d + 1) * 4);
+}
+
+extern "C" fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* block_tables,
+                               const int* seq_lens, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                               int B, int H, int Hkv, int Nq, int d, int block_size, int max_blocks, float scale,
+                               int causal, int in_dtype, int o_dtype, void* stream) {
+    // ---- validation: no HIP call before it passes
+    if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !o || !workspace) return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || Hkv < 1 || Nq < 1 || d < 1 || max_blocks < 1) return FA_ERR_INVALID_ARG;
+    if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
+    if (block_size < 16 || block_size > (1 << 20) || (block_size & (block_size - 1)) != 0) return FA_ERR_INVALID_ARG;
+    if (in_dtype != FA_BF16 && in_dtype != FA_F32) return FA_ERR_INVALID_ARG;
+    if (o_dtype != FA_BF16 && o_dtype != FA_F32) return FA_ERR_INVALID_ARG;
+    if (!aligned_d(q, 16) || !aligned_d(k_cache, 16) || !aligned_d(v_cache, 16) || !aligned_d(o, 16) ||
+        !aligned_d(workspace, 16) || !aligned_d(block_tables, 4) || !aligned_d(seq_lens, 4))
+        return FA_ERR_INVALID_ARG;
+    if (lse && !aligned_d(lse, 4)) return FA_ERR_INVALID_ARG;
+    if (scale != scale || fabsf(scale) == INFINITY) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    const long long max_len = (long long)max_blocks * block_size;
+    if (max_len > INT32_MAX / 2) return FA_ERR_UNSUPPORTED;
+    const size_t need = fa_decode_workspace_bytes(B, H, Hkv, Nq, d, (int)max_len);
+    if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+    const int S = decode_splits(B, H, Hkv, Nq, (int)max_len);
+    const long long G = (long long)(H / Hkv) * Nq;
+    const long long n_rt = (G + 31) / 32;
+    const long long items = (long long)B * Hkv * n_rt * S;
+    const long long rows = (long long)B * H * Nq;
+    if (items > INT32_MAX || (items + 3) / 4 > INT32_MAX || (rows + 3) / 4 > INT32_MAX) return FA_ERR_UNSUPPORTED;
+
+    if (scale < 0.f) scale = 1.0f / sqrtf((float)d);
+    DecodeParams p;
+    p.q = q; p.k_cache = k_cache; p.v_cache = v_cache; p.block_tables = block_tables; p.seq_lens = seq_lens;
+    p.part_o = (float*)workspace;
+    p.part_lse = (float*)workspace + rows * S * d;
+    p.o = o; p.lse = lse;
+    p.B = B; p.H = H; p.Hkv = Hkv; p.Nq = Nq;
+    p.group = H / Hkv; p.G = (int)G; p.n_rt = (int)n_rt; p.S = S;
+    const long long per = (max_len + S - 1) / S;
+    p.chunk = (int)((per + 31) / 32 * 32);
+    int lg = 0;
+    while ((1 << lg) < block_size) ++lg;
+    p.bs_log2 = lg;
+    p.max_blocks = max_blocks;
+    p.scale_log2 = scale > 0.f ? scale * kLog2e : 1e-30f;
+
+    hipStream_t s = (hipStream_t)stream;
+    const unsigned g1 = (unsigned)((items + 3) / 4), g2 = (unsigned)((rows + 3) / 4);
+    const bool c = causal != 0, ob = o_dtype == FA_BF16;
+    if (d == 128) {
+        if (c) hipLaunchKernelGGL((fa_decode_split_kernel<128, true>), dim3(g1), dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((fa_decode_split_kernel<128, false>), dim3(g1), dim3(256), 0, s, p);
+    } else {
+        if (c) hipLaunchKernelGGL((fa_decode_split_kernel<64, true>), dim3(g1), dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((fa_decode_split_kernel<64, false>), dim3(g1), dim3(256), 0, s, p);
+    }
+    if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+    if (d == 128) {
+        if (ob) hipLaunchKernelGGL((fa_decode_merge_kernel<128, true>), dim3(g2), dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((fa_decode_merge_kernel<128, false>), dim3(g2), dim3(256), 0, s, p);
+    } else {
+        if (ob) hipLaunchKernelGGL((fa_decode_merge_kernel<64, true>), dim3(g2), dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((fa_decode_merge_kernel<64, false>), dim3(g2), dim3(256), 0, s, p);
+    }
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}

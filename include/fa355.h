@@ -23,6 +23,8 @@
 #ifndef FA355_H
 #define FA355_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -160,6 +162,52 @@ FA355_API fa_status fa_bwd(const void* q, const void* k, const void* v, const vo
                            const float* lse, float* dq, float* dk, float* dv, float* delta,
                            int B, int H, int Nq, int Nk, int d, float scale, int causal,
                            int layout, int in_dtype, int o_dtype, void* stream);
+
+/*
+ * fa_decode -- enqueue decode attention over a paged KV cache on `stream`.
+ *
+ * The operation: Nq new tokens of each of B sequences attend to the
+ * sequence's cached keys and values.  Token t of sequence b sits at position
+ * L_b - Nq + t (L_b = seq_lens[b]); key j < L_b is visible to it (causal: j <=
+ * L_b - Nq + t).  O and LSE are those of fa_fwd over the visible keys.  The
+ * cache is paged as [nanhubrain] "GatherPAKVCache" describes: logical block i
+ * of sequence b is physical block block_tables[b][i], and query head h reads
+ * key/value head h / (H / Hkv).  The kernels read the blocks in place (no
+ * gathered copy), split each sequence's keys into chunks, and merge the
+ * chunks' partial results with the online-softmax merge
+ * (LSE = log sum_s exp LSE_s, O = sum_s exp(LSE_s - LSE) O_s).
+ *
+ * q            device, [B, Nq, H, d] bf16 (the new tokens' queries).
+ * k_cache,
+ * v_cache      device, [num_blocks, block_size, Hkv, d] bf16.
+ * block_tables device, int32 [B, max_blocks]: physical block ids; the first
+ *              ceil(L_b / block_size) entries of row b must be valid blocks.
+ * seq_lens     device, int32 [B]: L_b, 0 <= L_b <= max_blocks * block_size
+ *              (values outside are clamped to that range); causal needs
+ *              L_b >= Nq (a token at a negative position sees no key).
+ * o            device, [B, Nq, H, d], element type `o_dtype`.
+ * lse          device, float32 [B, H, Nq], natural log; NULL = not written.
+ *              A row with no visible key (L_b = 0) gets O = 0, LSE = -inf.
+ * workspace    device, at least fa_decode_workspace_bytes(B, H, Hkv, Nq, d,
+ *              max_blocks * block_size) bytes, 16-byte aligned, caller-owned;
+ *              holds the chunks' partial results (overwritten).
+ * block_size   tokens per block, a power of two >= 16.
+ * scale        as for fa_fwd (negative: 1/sqrt(d)).
+ * in_dtype     FA_BF16 (FA_F32 is FA_ERR_UNSUPPORTED); o_dtype FA_F32 or FA_BF16.
+ *
+ * Errors: FA_ERR_INVALID_ARG for null pointers, sizes < 1, H % Hkv != 0, a
+ * block size that is not a power of two >= 16, misalignment, NaN/inf scale or
+ * a workspace below the required size; FA_ERR_UNSUPPORTED for d not 64/128.
+ * The library allocates nothing; two kernels are enqueued, no synchronisation.
+ */
+FA355_API fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* block_tables,
+                              const int* seq_lens, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                              int B, int H, int Hkv, int Nq, int d, int block_size, int max_blocks, float scale,
+                              int causal, int in_dtype, int o_dtype, void* stream);
+
+/* Workspace bytes fa_decode needs for these sizes (max_seq_len = max_blocks *
+ * block_size); 0 for invalid sizes. */
+FA355_API size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int Nq, int d, int max_seq_len);
 
 /* A static, human-readable name for a status code (never NULL). */
 FA355_API const char* fa_status_str(int status);

@@ -41,6 +41,8 @@ def decode_reference(lib, q, key_cache, value_cache, block_tables, seq_lens, *, 
     lse = np.full((B, H, Nq), -np.inf)
     for b in range(B):
         L = int(seq_lens[b])
+        if causal and L < Nq:
+            raise ValueError("causal decode needs every sequence to hold its Nq new tokens")
         if L == 0:
             continue
         k, v = gather_paged_kv(key_cache, value_cache, block_tables[b], L)

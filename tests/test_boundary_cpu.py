@@ -187,3 +187,41 @@ def xcall(**changes):
 ])
 def test_fwd_ex_validation_returns_before_launch(changes, status):
     assert xcall(**changes) == status
+
+
+DGOOD = dict(q=P, kc=P + 0x1000, vc=P + 0x2000, bt=P + 0x3000, sl=P + 0x4000, o=P + 0x5000, lse=P + 0x6000,
+             ws=P + 0x7000, ws_bytes=1 << 30, B=2, H=4, Hkv=2, Nq=1, d=128, bs=16, mb=8, scale=-1.0, causal=0,
+             in_dtype=fa.FA_BF16, o_dtype=fa.FA_F32, stream=None)
+
+
+def dcall(**changes):
+    a = dict(DGOOD, **changes)
+    return fa.fa_decode(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["o"], a["lse"], a["ws"], a["ws_bytes"],
+                        a["B"], a["H"], a["Hkv"], a["Nq"], a["d"], a["bs"], a["mb"], a["scale"], a["causal"],
+                        a["in_dtype"], a["o_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("changes,status", [
+    *[(dict(**{name: 0}), fa.FA_ERR_INVALID_ARG) for name in ("q", "kc", "vc", "bt", "sl", "o", "ws")],
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=6, Hkv=4), fa.FA_ERR_INVALID_ARG),
+    (dict(bs=24), fa.FA_ERR_INVALID_ARG),          # not a power of two
+    (dict(bs=8), fa.FA_ERR_INVALID_ARG),           # below 16
+    (dict(mb=0), fa.FA_ERR_INVALID_ARG),
+    (dict(bt=P + 0x3002), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=P + 0x7008), fa.FA_ERR_INVALID_ARG),
+    (dict(ws_bytes=16), fa.FA_ERR_INVALID_ARG),    # workspace too small
+    (dict(scale=math.inf), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(in_dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+])
+def test_decode_validation_returns_before_launch(changes, status):
+    assert dcall(**changes) == status
+
+
+def test_decode_workspace_formula():
+    # B*H*Nq*S*(d+1) floats with S = min(ceil(2048 / (B*Hkv*row tiles)), ceil(max_len / 256))
+    assert fa.fa_decode_workspace_bytes(2, 4, 2, 1, 128, 128) == 2 * 4 * 1 * 1 * 129 * 4
+    assert fa.fa_decode_workspace_bytes(2, 4, 2, 1, 128, 100000) == 2 * 4 * 1 * 391 * 129 * 4
+    assert fa.fa_decode_workspace_bytes(32, 32, 8, 1, 128, 8192) == 32 * 32 * 8 * 129 * 4
+    assert fa.fa_decode_workspace_bytes(0, 4, 2, 1, 128, 128) == 0
