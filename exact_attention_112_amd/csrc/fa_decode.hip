@@ -81,11 +81,13 @@ void fa_decode_split_kernel(DecodeParams p) {
     const int total = p.B * p.Hkv * p.n_rt * p.S;
     const int item = __builtin_amdgcn_workgroup_id_x() * NWV + wave;
     if (item >= total) return;                       // whole wave; no barriers below
+    // KV head fastest: the waves of a workgroup read the same tokens of
+    // neighbouring heads (one token's heads are contiguous in the cache)
     int rest = item;
-    const int s = rest % p.S; rest /= p.S;
+    const int hk = rest % p.Hkv; rest /= p.Hkv;
     const int rt = rest % p.n_rt; rest /= p.n_rt;
-    const int hk = rest % p.Hkv;
-    const int b = rest / p.Hkv;
+    const int s = rest % p.S;
+    const int b = rest / p.S;
 
     const int cap = p.max_blocks << p.bs_log2;
     const int L = min(max(p.seq_lens[b], 0), cap);
