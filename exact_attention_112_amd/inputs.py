@@ -53,6 +53,7 @@ class Workload:
     peaked_mult: float = 8.0
     Hkv: int = 0               # key/value heads (0: H); query head h reads KV head h // (H // Hkv)
     window: tuple = (-1, -1)   # band (left, right): keys i-left .. i+right visible; negative: unbounded
+    block_sparse: bool = False  # a block mask from make_block_mask decides which key blocks are computed
 
     @property
     def kv_heads(self) -> int:
@@ -115,7 +116,37 @@ WORKLOADS = {
     # ([pwwt] pre_tokens / next_tokens), at the LLaMA-like 32 x 128 head shape
     "gqa_swa_prefill": Workload(6, "gqa_swa_prefill", 1, 32, 16384, 16384, 128, "bf16", "BSND", True,
                                 Hkv=8, window=(4095, -1)),
+    # block-sparse attention of the BigBird kind ([nanhubrain] "SparseFlashAttention"):
+    # local, global and random key blocks per query block
+    "sparse_bigbird": Workload(8, "sparse_bigbird", 2, 16, 16384, 16384, 128, "bf16", "BHND", False,
+                               block_sparse=True),
 }
+
+# granularity of block masks: queries x keys per block
+SPARSE_BQ, SPARSE_BK = 256, 64
+
+
+def make_block_mask(w: Workload, seed_base: int | None = None, n_random: int = 8) -> np.ndarray:
+    """uint8 [B, H, ceil(Nq/256), ceil(Nk/64)]: for each (b, h) and query block
+    qb, the key blocks overlapping keys [256*qb - 256, 256*qb + 512) (local),
+    the first 4 key blocks (global) and n_random key blocks drawn from seed
+    1000*cid+7 (random), the BigBird pattern."""
+    base = 1000 * w.cid if seed_base is None else seed_base
+    nqb = (w.Nq + SPARSE_BQ - 1) // SPARSE_BQ
+    nkb = (w.Nk + SPARSE_BK - 1) // SPARSE_BK
+    g = np.random.Generator(np.random.PCG64(base + 7))
+    mask = np.zeros((w.B, w.H, nqb, nkb), dtype=np.uint8)
+    for qb in range(nqb):
+        lo = max(0, (SPARSE_BQ * qb - SPARSE_BQ) // SPARSE_BK)
+        hi = min(nkb, (SPARSE_BQ * qb + 2 * SPARSE_BQ + SPARSE_BK - 1) // SPARSE_BK)
+        mask[:, :, qb, lo:hi] = 1
+        mask[:, :, qb, :min(4, nkb)] = 1
+    rnd = g.integers(0, nkb, size=(w.B, w.H, nqb, n_random))
+    for b in range(w.B):
+        for h in range(w.H):
+            for qb in range(nqb):
+                mask[b, h, qb, rnd[b, h, qb]] = 1
+    return mask
 BY_ID = {w.cid: w for w in WORKLOADS.values()}
 
 

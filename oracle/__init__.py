@@ -6,7 +6,8 @@ Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 it shares no code with the GPU path (the only common module is the seeded
 input generator, which holds none of the method's arithmetic).
 
-Four implementations live here:
+Four implementations live here (plus the paged-cache and block-sparse
+references in paged.py and sparse.py):
 
 * ``attn_fwd`` -- the plain definition, a two-pass fp64 softmax attention in C
   (``oracle.c``): scores, row max, exp-sum, weighted sum of values, one row at
