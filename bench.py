@@ -180,6 +180,45 @@ def cpu_baseline_bwd(w, inp, grad, target_s: float = 10.0):
     }
 
 
+def sparse_pair_flops(w, mask) -> float:
+    """4*d per (query, key) pair the block mask lets through (no causal here)."""
+    import numpy as np
+    rows = np.minimum(256, w.Nq - 256 * np.arange(mask.shape[2]))
+    cols = np.minimum(64, w.Nk - 64 * np.arange(mask.shape[3]))
+    pairs = float(np.einsum("bhqk,q,k->", mask.astype(np.float64), rows.astype(np.float64),
+                            cols.astype(np.float64)))
+    return 4.0 * w.d * pairs
+
+
+def cpu_baseline_sparse(w, inp, mask, target_s: float = 10.0):
+    """Time the block-sparse oracle (numpy fp64) on every 16th query row of
+    consecutive heads until ``target_s`` seconds are done."""
+    import numpy as np
+    from oracle import sparse
+
+    rows = np.arange(0, w.Nq, 16)
+    done, elapsed, flops = 0, 0.0, 0.0
+    bh = (lambda x: x) if w.layout == "BHND" else (lambda x: x.transpose(0, 2, 1, 3))
+    Q, K, V = bh(inp.q), bh(inp.k), bh(inp.v)
+    while done < w.B * w.H and elapsed < target_s:
+        b, h = divmod(done, w.H)
+        t0 = time.perf_counter()
+        sparse.attn_fwd_block_sparse(Q[b, h], K[b, h], V[b, h], mask[b, h], bq=256, bk=64, scale=w.scale,
+                                     causal=w.causal, rows=rows)
+        elapsed += time.perf_counter() - t0
+        cols = np.minimum(64, w.Nk - 64 * np.arange(mask.shape[3]))
+        flops += 4.0 * w.d * float(sum((mask[b, h, r // 256] * cols).sum() for r in rows))
+        done += 1
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"numpy fp64 block-sparse oracle on every 16th query row of the first {done} of {w.B * w.H} "
+                   f"heads of {w.name}; {flops:.3e} flop in {elapsed:.1f} s"),
+    }
+
+
 def decode_bytes(w, lens) -> float:
     """Algorithmic bytes of one decode call: every cached K and V row of every
     sequence read once (bf16), Q read and O (fp32) and LSE written once, the
@@ -333,9 +372,15 @@ def main(argv=None):
     o = torch.empty(tq.shape, dtype=out_dtype, device="cuda")
     lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
 
+    bmask, sparse_flops = None, None
+    if w.block_sparse:
+        mask_np = I.make_block_mask(w)
+        bmask = torch.from_numpy(mask_np).to("cuda")
+        sparse_flops = sparse_pair_flops(w, mask_np)
+
     def step():
         fa.fwd(tq, tk, tv, causal=w.causal, scale=w.scale, layout=w.layout, out_dtype=out_dtype,
-               out=o, lse=lse, window=None if w.window == (-1, -1) else w.window)
+               out=o, lse=lse, window=None if w.window == (-1, -1) else w.window, block_mask=bmask)
 
     if args.which == "bwd":
         if w.dtype != "bf16" or w.kv_heads != w.H or w.window != (-1, -1):
@@ -369,7 +414,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     bwd = args.which == "bwd"
-    flops = 2.5 * w.flops if bwd else w.flops
+    flops = 2.5 * w.flops if bwd else (sparse_flops if w.block_sparse else w.flops)
     tflops = flops / (ms * 1e-3) / 1e12
     outs = (dq, dk, dv) if bwd else (o, lse)
     if not all(torch.isfinite(t).all() for t in outs):
@@ -379,7 +424,12 @@ def main(argv=None):
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline_bwd(w, inp, grad_vals) if bwd else cpu_baseline(w, inp)
+        if bwd:
+            cpu = cpu_baseline_bwd(w, inp, grad_vals)
+        elif w.block_sparse:
+            cpu = cpu_baseline_sparse(w, inp, mask_np)
+        else:
+            cpu = cpu_baseline(w, inp)
 
     traffic = traffic_from_profiles(w.name, args.which)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -404,12 +454,16 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": ("synthetic (seeded N(0,1) Q/K/V/dO of the workload's shape; O, LSE from the GPU forward)"
+        "data": ("synthetic (seeded N(0,1) Q/K/V of the workload's shape, seeded BigBird-like block mask)"
+                 if w.block_sparse else
+                 "synthetic (seeded N(0,1) Q/K/V/dO of the workload's shape; O, LSE from the GPU forward)"
                  if bwd else "synthetic (seeded N(0,1) Q/K/V of the workload's shape)"),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                    "causal": w.causal, "layout": w.layout, "out_dtype": args.out_dtype,
                    **({"Hkv": w.kv_heads, "window": list(w.window)}
                       if w.kv_heads != w.H or w.window != (-1, -1) else {}),
+                   **({"block_sparse": True, "mask_density": round(float(mask_np.mean()), 4)}
+                      if w.block_sparse else {}),
                    **({"pass": "bwd", "grads": "f32"} if bwd else {})},
         "roofline": roof,
         "cpu_baseline": cpu,

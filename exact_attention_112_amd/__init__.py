@@ -34,7 +34,7 @@ FA_BF16, FA_F32 = 0, 1
 LAYOUTS = {"BHND": FA_BHND, "BSND": FA_BSND}
 
 # the symbols include/fa355.h declares
-EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_decode", "fa_decode_workspace_bytes", "fa_status_str",
+EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_sparse", "fa_bwd", "fa_decode", "fa_decode_workspace_bytes", "fa_status_str",
            "fa_abi_version")
 ABI_VERSION = 1
 
@@ -73,6 +73,9 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.fa_fwd_ex.restype = ctypes.c_int
     lib.fa_fwd_ex.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [ctypes.c_float]
                               + [ctypes.c_int] * 6 + [ctypes.c_void_p])
+    lib.fa_fwd_sparse.restype = ctypes.c_int
+    lib.fa_fwd_sparse.argtypes = ([ctypes.c_void_p] * 6 + [ctypes.c_int] * 5 + [ctypes.c_float]
+                                  + [ctypes.c_int] * 4 + [ctypes.c_void_p])
     lib.fa_decode.restype = ctypes.c_int
     lib.fa_decode.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.c_size_t] + [ctypes.c_int] * 7 + [ctypes.c_float]
                               + [ctypes.c_int] * 3 + [ctypes.c_void_p])
@@ -112,14 +115,27 @@ def fa_fwd_ex(q: int, k: int, v: int, o: int, lse: int | None, B: int, H: int, H
                                 int(o_dtype), stream or None))
 
 
+def fa_fwd_sparse(q: int, k: int, v: int, o: int, lse: int | None, block_mask: int, B: int, H: int, Nq: int,
+                  Nk: int, d: int, scale: float, causal: int, layout: int, in_dtype: int, o_dtype: int,
+                  stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the fa_status."""
+    return int(load().fa_fwd_sparse(q, k, v, o, lse or None, block_mask, B, H, Nq, Nk, d, float(scale),
+                                    int(causal), int(layout), int(in_dtype), int(o_dtype), stream or None))
+
+
+SPARSE_BQ, SPARSE_BK = 256, 64
+
+
 def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, layout: str = "BHND",
-        out_dtype=None, out=None, lse=None, return_lse: bool = True, window=None):
+        out_dtype=None, out=None, lse=None, return_lse: bool = True, window=None, block_mask=None):
     """Attention forward on torch CUDA tensors (ROCm).
 
     q: [B,H,Nq,d] (BHND) or [B,Nq,H,d] (BSND); k, v: same with Nk and Hkv
     heads, Hkv dividing H (grouped-query attention when Hkv < H).  bf16 or
     fp32, contiguous, on one GPU.  ``window=(left, right)``: key j visible to
     query i iff i-left <= j <= i+right (a negative side is unbounded).
+    ``block_mask``: uint8 [B, H, ceil(Nq/256), ceil(Nk/64)] GPU tensor; key
+    block j//64 is computed for query block i//256 iff its entry is nonzero.
     Returns (O, LSE): O in q's layout with dtype ``out_dtype`` (default
     float32), LSE float32 [B,H,Nq].  The kernel is enqueued on the current
     stream.
@@ -167,7 +183,16 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, layout: st
     with torch.cuda.device(q.device):
         sc = -1.0 if scale is None else float(scale)
         lp = lse.data_ptr() if lse is not None else None
-        if Hk == H and wl < 0 and wr < 0:
+        if block_mask is not None:
+            nqb, nkb = (Nq + SPARSE_BQ - 1) // SPARSE_BQ, (Nk + SPARSE_BK - 1) // SPARSE_BK
+            if (block_mask.shape != (B, H, nqb, nkb) or block_mask.dtype != torch.uint8
+                    or not block_mask.is_contiguous() or block_mask.device != q.device):
+                raise ValueError(f"block_mask must be a contiguous uint8 [{B},{H},{nqb},{nkb}] tensor on q's device")
+            if Hk != H or wl >= 0 or wr >= 0:
+                raise ValueError("block_mask does not combine with grouped KV heads or a window")
+            st = fa_fwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lp, block_mask.data_ptr(),
+                               B, H, Nq, Nk, d, sc, int(bool(causal)), LAYOUTS[layout], in_dt, o_dt, stream)
+        elif Hk == H and wl < 0 and wr < 0:
             st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lp, B, H, Nq, Nk, d,
                         sc, int(bool(causal)), LAYOUTS[layout], in_dt, o_dt, stream)
         else:

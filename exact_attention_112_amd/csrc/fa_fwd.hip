@@ -72,7 +72,13 @@ struct FwdParams {
     float scale_log2;             // scale * log2(e)
     int group;                    // query heads per key/value head (H / Hkv)
     int wl, wr;                   // band: keys i-wl .. i+wr visible (negative: unbounded)
+    const unsigned char* block_mask;  // block-sparse: [B*H][n_qb][n_kb], nonzero = computed
+    int n_qb, n_kb;               // mask blocks: 256 queries x 64 keys
 };
+
+// Variants of the bf16 forward kernel.
+enum : int { kPlain = 0, kBand = 1, kSparse = 2 };
+constexpr int kMaxSparseTiles = 4096;   // key tiles of 64 a block-sparse launch may list
 
 // ---------------------------------------------------------------------------
 // bf16 kernel
@@ -317,12 +323,15 @@ struct Bf16Cfg {
     static_assert(TILE_CH % (64 * NW) == 0, "tile must split evenly over the waves");
 };
 
-// BAND: keys outside the band i-wl .. i+wr are masked and the tiles outside
-// the workgroup's band are never loaded; rows may see no key at all (O = 0,
-// LSE = -inf).
-template <int D, int NW, bool CAUSAL, bool OUT_BF16, bool BAND>
+// MODE kBand: keys outside the band i-wl .. i+wr are masked and the tiles
+// outside the workgroup's band are never loaded.  MODE kSparse: the key
+// tiles a block mask marks off for the workgroup's 256 queries are never
+// loaded; the workgroup runs over the sorted list of the others.  In both,
+// rows may see no key at all (O = 0, LSE = -inf).
+template <int D, int NW, bool CAUSAL, bool OUT_BF16, int MODE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_kernel(FwdParams p) {
+    constexpr bool BAND = MODE == kBand, SPARSE = MODE == kSparse, SAFE = MODE != kPlain;
     using C = Bf16Cfg<D, NW>;
     constexpr int BC = C::BC, BR = C::BR, DCH = C::DCH, TILE_CH = C::TILE_CH, TB = C::TILE_BYTES;
     constexpr int LPW = C::LPW, KK = D / 16, DB = D / 32;
@@ -395,6 +404,43 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         hi_key = min(Nk - 1, wr >= 0 ? q + wr : big);
         if (CAUSAL) hi_key = min(hi_key, q);
     }
+    // Block-sparse: the workgroup walks the sorted list of its unmasked-off
+    // tiles; "tile" v below is then list entry v.  The tiles a wave or the
+    // whole workgroup sees in full are a prefix of the list (the list is
+    // sorted and only the diagonal / last tiles need a mask).
+    __shared__ unsigned short tile_list[SPARSE ? kMaxSparseTiles : 1];
+    __shared__ int list_len;
+    if constexpr (SPARSE) {
+        const unsigned char* mrow = p.block_mask + ((long long)bh * p.n_qb + qt) * p.n_kb;
+        if (wave == 0) {
+            int count = 0;
+            for (int base = 0; base < n_kt; base += 64) {
+                const int t = base + lane;
+                const bool on = t < n_kt && mrow[t] != 0;
+                const unsigned long long bal = __builtin_amdgcn_ballot_w64(on);
+                const int pos = count + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
+                                                                      __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+                if (on) tile_list[pos] = (unsigned short)t;
+                count += __builtin_popcountll(bal);
+            }
+            if (lane == 0) list_len = count;
+        }
+        __syncthreads();
+        const int n_list = list_len;
+        int v_full = 0, v_wave = 0;
+        for (int base = 0; base < n_list; base += 64) {
+            const int v = base + lane;
+            const int t = v < n_list ? (int)tile_list[v] : (1 << 30);
+            v_full += __builtin_popcountll(__builtin_amdgcn_ballot_w64(t < n_full));
+            v_wave += __builtin_popcountll(__builtin_amdgcn_ballot_w64(t < n_kt_wave));
+        }
+        n_kt = n_list;
+        n_full = v_full;
+        n_kt_wave = v_wave;
+        lo_key = -(1 << 30);
+        hi_key = CAUSAL ? min(Nk - 1, q) : Nk - 1;
+    }
+#define FA_TILE(v) (SPARSE ? (int)tile_list[(v)] : (v))
 
     // ---- Q fragment (B operand of S^T = K Q^T): lane holds Q[q][16kk + 8hi .. +7]
     bf16x8 qreg[KK];
@@ -431,10 +477,12 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // tile t lives in stage (t - t_begin) % 2 (t_begin = 0 without a band)
 #define FA_K_STAGE(t) (lds + (((t) - t_begin) & 1) * TB)
 #define FA_V_STAGE(t) (lds + (2 + (((t) - t_begin) & 1)) * TB)
-#define FA_ISSUE_K(t) issue_tile<LPW, DCH, BC, NW>(kaddr + (unsigned long long)(t) * tile_bytes, rb, ld_koff, \
-                                              ldst + (((t) - t_begin) & 1) * TB, Nk - (t) * BC, wave, lane)
-#define FA_ISSUE_V(t) issue_tile<LPW, DCH, BC, NW>(vaddr + (unsigned long long)(t) * tile_bytes, rb, ld_voff, \
-                                              ldst + (2 + (((t) - t_begin) & 1)) * TB, Nk - (t) * BC, wave, lane)
+#define FA_ISSUE_K(t) issue_tile<LPW, DCH, BC, NW>(kaddr + (unsigned long long)FA_TILE(t) * tile_bytes, rb, \
+                                              ld_koff, ldst + (((t) - t_begin) & 1) * TB, Nk - FA_TILE(t) * BC, \
+                                              wave, lane)
+#define FA_ISSUE_V(t) issue_tile<LPW, DCH, BC, NW>(vaddr + (unsigned long long)FA_TILE(t) * tile_bytes, rb, \
+                                              ld_voff, ldst + (2 + (((t) - t_begin) & 1)) * TB,              \
+                                              Nk - FA_TILE(t) * BC, wave, lane)
 
     RowState<D> st;
 #pragma unroll
@@ -459,7 +507,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // read: K tile j+2 and V tile j+1; then computes P_j, O += P_j V_j and
     // the scores of tile j+1.
     f32x16 sa[2], sb[2];   // scores of the current / next tile (roles alternate)
-    if (!BAND || n_kt > 0) {
+    if (!SAFE || n_kt > 0) {
         FA_ISSUE_K(t_begin);
         FA_ISSUE_V(t_begin);
         if (t_begin + 1 < n_kt) FA_ISSUE_K(t_begin + 1);
@@ -469,8 +517,9 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         // Scores of the first tile.  Without a band every row (padding rows
         // included: their Q is zero) sees key 0, so the first max is finite.
         qk_tile<D>(sa, qreg, (const u32x4*)FA_K_STAGE(t_begin), col, hi);
-        if constexpr (BAND) {
-            if (t_begin < t_full_lo || t_begin >= n_full) mask_tile_band(sa, t_begin * BC, lo_key, hi_key, hi);
+        if constexpr (SAFE) {
+            if (t_begin < t_full_lo || t_begin >= n_full)
+                mask_tile_band(sa, FA_TILE(t_begin) * BC, lo_key, hi_key, hi);
         } else {
             if (n_full == 0) mask_tile<CAUSAL>(sa, 0, q, Nk, hi);
         }
@@ -507,21 +556,21 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // score buffers swap roles without copies.
     for (; j + 2 < n_full; j += 2) {
         FA_TOP(j);
-        wave_step<D, CAUSAL, false, true>(st, sa, sb, qreg, FA_KS(j + 1), FA_V_STAGE(j), (j + 1) * BC, q, Nk,
-                                                 sl2, col, hi, tr_row, tr_dd);
+        wave_step<D, CAUSAL, false, true>(st, sa, sb, qreg, FA_KS(j + 1), FA_V_STAGE(j), 0, q, Nk, sl2, col, hi,
+                                          tr_row, tr_dd);
         FA_TOP(j + 1);
-        wave_step<D, CAUSAL, false, true>(st, sb, sa, qreg, FA_KS(j + 2), FA_V_STAGE(j + 1), (j + 2) * BC, q,
-                                                 Nk, sl2, col, hi, tr_row, tr_dd);
+        wave_step<D, CAUSAL, false, true>(st, sb, sa, qreg, FA_KS(j + 2), FA_V_STAGE(j + 1), 0, q, Nk, sl2, col,
+                                          hi, tr_row, tr_dd);
     }
     // The remaining steps (at most a few): masks on, per-wave skips, no
     // overlap (one score buffer).
     for (; j < n_kt; ++j) {
         FA_TOP(j);
         if (j < n_kt_wave) {
-            if constexpr (BAND) {
+            if constexpr (SAFE) {
                 if (j + 1 < n_kt_wave)
-                    wave_step_band<D, true>(st, sa, qreg, FA_KS(j + 1), FA_V_STAGE(j), (j + 1) * BC, lo_key, hi_key,
-                                            sl2, col, hi, tr_row, tr_dd);
+                    wave_step_band<D, true>(st, sa, qreg, FA_KS(j + 1), FA_V_STAGE(j), FA_TILE(j + 1) * BC, lo_key,
+                                            hi_key, sl2, col, hi, tr_row, tr_dd);
                 else
                     wave_step_band<D, false>(st, sa, qreg, nullptr, FA_V_STAGE(j), 0, lo_key, hi_key, sl2, col, hi,
                                              tr_row, tr_dd);
@@ -542,6 +591,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 #undef FA_ISSUE_V
 #undef FA_TOP
 #undef FA_KS
+#undef FA_TILE
 
     // ---- epilogue
     const float l_tot = pair_sum(st.l0 + st.l1);
@@ -549,7 +599,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     const int hi_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5;
     if (q < Nq) {
         // (band: a row that saw no key has l = 0 and gets O = 0, LSE = -inf)
-        const float inv = (!BAND || l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+        const float inv = (!SAFE || l_tot > 0.f) ? 1.0f / l_tot : 0.f;
         char* obase = (char*)p.o;
         const long long orow = (long long)b * p.q_sb + (long long)h * p.q_sh + (long long)q * p.q_sn;
 #pragma unroll
@@ -567,7 +617,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
                 }
             }
         if (p.lse && hi_e == 0)
-            p.lse[(long long)bh * Nq + q] = (!BAND || l_tot > 0.f) ? (st.m + __builtin_amdgcn_logf(l_tot)) * kLn2
+            p.lse[(long long)bh * Nq + q] = (!SAFE || l_tot > 0.f) ? (st.m + __builtin_amdgcn_logf(l_tot)) * kLn2
                                                                    : -INFINITY;
     }
 }
@@ -725,12 +775,15 @@ constexpr int kWavesBf16 = FA_WAVES_BF16;   // queries per workgroup = 32 * wave
 constexpr int kWavesF32 = 4;
 
 template <int D, bool CAUSAL, bool OUT_BF16>
-hipError_t launch_bf16(const FwdParams& p, int grid, bool band, hipStream_t s) {
-    if (band)
-        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, kWavesBf16, CAUSAL, OUT_BF16, true>), dim3(grid),
+hipError_t launch_bf16(const FwdParams& p, int grid, int mode, hipStream_t s) {
+    if (mode == kBand)
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, kWavesBf16, CAUSAL, OUT_BF16, kBand>), dim3(grid),
+                           dim3(kWavesBf16 * 64), 0, s, p);
+    else if (mode == kSparse)
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, kWavesBf16, CAUSAL, OUT_BF16, kSparse>), dim3(grid),
                            dim3(kWavesBf16 * 64), 0, s, p);
     else
-        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, kWavesBf16, CAUSAL, OUT_BF16, false>), dim3(grid),
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, kWavesBf16, CAUSAL, OUT_BF16, kPlain>), dim3(grid),
                            dim3(kWavesBf16 * 64), 0, s, p);
     return hipGetLastError();
 }
@@ -757,10 +810,11 @@ extern "C" const char* fa_status_str(int status) {
     }
 }
 
-extern "C" fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
-                               int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
-                               int window_left, int window_right, int layout, int in_dtype, int o_dtype,
-                               void* stream) {
+namespace {
+
+fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, const unsigned char* block_mask,
+                   int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int window_left,
+                   int window_right, int layout, int in_dtype, int o_dtype, void* stream) {
     // ---- validation: no HIP call before it passes
     if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARG;
@@ -775,7 +829,9 @@ extern "C" fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void
     if (in_dtype == FA_F32 && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
     const bool band = window_left >= 0 || window_right >= 0;
     // the fp32 kernel serves plain attention only
-    if (in_dtype == FA_F32 && (band || Hkv != H)) return FA_ERR_UNSUPPORTED;
+    if (in_dtype == FA_F32 && (band || Hkv != H || block_mask)) return FA_ERR_UNSUPPORTED;
+    if (block_mask && (band || (Nk + 63) / 64 > kMaxSparseTiles)) return FA_ERR_UNSUPPORTED;
+    const int mode = block_mask ? kSparse : band ? kBand : kPlain;
 
     const int rows_per_wg = 32 * (in_dtype == FA_BF16 ? kWavesBf16 : kWavesF32);
     const long long n_qtiles = ((long long)Nq + rows_per_wg - 1) / rows_per_wg;
@@ -804,6 +860,9 @@ extern "C" fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void
     p.group = H / Hkv;
     p.wl = window_left < 0 ? -1 : window_left;
     p.wr = window_right < 0 ? -1 : window_right;
+    p.block_mask = block_mask;
+    p.n_qb = (int)n_qtiles;          // mask rows: the kernel's 256-query tiles
+    p.n_kb = (Nk + 63) / 64;
     // scale 0 (uniform weights) runs as a tiny positive scale: every scaled
     // score is then below 2^-24 in magnitude and every probability rounds to
     // exactly 1, as with scale 0, while masked (-inf) scores still give 0.
@@ -816,11 +875,11 @@ extern "C" fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void
         const bool ob = o_dtype == FA_BF16;
         const int g = (int)grid;
         if (d == 128) {
-            err = c ? (ob ? launch_bf16<128, true, true>(p, g, band, s) : launch_bf16<128, true, false>(p, g, band, s))
-                    : (ob ? launch_bf16<128, false, true>(p, g, band, s) : launch_bf16<128, false, false>(p, g, band, s));
+            err = c ? (ob ? launch_bf16<128, true, true>(p, g, mode, s) : launch_bf16<128, true, false>(p, g, mode, s))
+                    : (ob ? launch_bf16<128, false, true>(p, g, mode, s) : launch_bf16<128, false, false>(p, g, mode, s));
         } else {
-            err = c ? (ob ? launch_bf16<64, true, true>(p, g, band, s) : launch_bf16<64, true, false>(p, g, band, s))
-                    : (ob ? launch_bf16<64, false, true>(p, g, band, s) : launch_bf16<64, false, false>(p, g, band, s));
+            err = c ? (ob ? launch_bf16<64, true, true>(p, g, mode, s) : launch_bf16<64, true, false>(p, g, mode, s))
+                    : (ob ? launch_bf16<64, false, true>(p, g, mode, s) : launch_bf16<64, false, false>(p, g, mode, s));
         }
     } else {
         if (d == 128) err = c ? launch_f32<128, true>(p, (int)grid, s) : launch_f32<128, false>(p, (int)grid, s);
@@ -829,9 +888,27 @@ extern "C" fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+}  // namespace
+
+extern "C" fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                               int window_left, int window_right, int layout, int in_dtype, int o_dtype,
+                               void* stream) {
+    return fwd_impl(q, k, v, o, lse, nullptr, B, H, Hkv, Nq, Nk, d, scale, causal, window_left, window_right,
+                    layout, in_dtype, o_dtype, stream);
+}
+
 extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int H, int Nq, int Nk, int d, float scale, int causal,
                             int layout, int in_dtype, int o_dtype, void* stream) {
-    return fa_fwd_ex(q, k, v, o, lse, B, H, H, Nq, Nk, d, scale, causal, -1, -1, layout, in_dtype, o_dtype,
-                     stream);
+    return fwd_impl(q, k, v, o, lse, nullptr, B, H, H, Nq, Nk, d, scale, causal, -1, -1, layout, in_dtype, o_dtype,
+                    stream);
+}
+
+extern "C" fa_status fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   const unsigned char* block_mask, int B, int H, int Nq, int Nk, int d, float scale,
+                                   int causal, int layout, int in_dtype, int o_dtype, void* stream) {
+    if (!block_mask) return FA_ERR_INVALID_ARG;
+    return fwd_impl(q, k, v, o, lse, block_mask, B, H, H, Nq, Nk, d, scale, causal, -1, -1, layout, in_dtype,
+                    o_dtype, stream);
 }

@@ -117,6 +117,27 @@ FA355_API fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void*
                               int window_left, int window_right, int layout, int in_dtype, int o_dtype,
                               void* stream);
 
+/* Granularity of fa_fwd_sparse's block mask: queries x keys per block. */
+#define FA_SPARSE_BQ 256
+#define FA_SPARSE_BK 64
+
+/*
+ * fa_fwd_sparse -- fa_fwd with a block-sparse mask ([nanhubrain]
+ * "SparseFlashAttention": a mask over (query block, key block) pairs; the
+ * key blocks it marks as not needed are skipped, never loaded nor computed).
+ *
+ * block_mask  device pointer, uint8 [B, H, ceil(Nq / FA_SPARSE_BQ),
+ *             ceil(Nk / FA_SPARSE_BK)] contiguous: key j is visible to query
+ *             i iff block_mask[b][h][i / 256][j / 64] != 0 (and j <= i if
+ *             causal).  A row with no visible key gets O = 0, LSE = -inf.
+ * All other arguments and rules are those of fa_fwd.  FA_ERR_INVALID_ARG for
+ * a NULL mask; FA_ERR_UNSUPPORTED for fp32 inputs or more than 4096 key
+ * blocks (Nk > 262144).
+ */
+FA355_API fa_status fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  const unsigned char* block_mask, int B, int H, int Nq, int Nk, int d,
+                                  float scale, int causal, int layout, int in_dtype, int o_dtype, void* stream);
+
 /*
  * fa_bwd -- enqueue the attention backward pass on `stream`: the gradients of
  * a loss L with respect to Q, K and V, given dO = dL/dO.

@@ -225,3 +225,31 @@ def test_decode_workspace_formula():
     assert fa.fa_decode_workspace_bytes(2, 4, 2, 1, 128, 100000) == 2 * 4 * 1 * 391 * 129 * 4
     assert fa.fa_decode_workspace_bytes(32, 32, 8, 1, 128, 8192) == 32 * 32 * 8 * 129 * 4
     assert fa.fa_decode_workspace_bytes(0, 4, 2, 1, 128, 128) == 0
+
+
+SGOOD = dict(GOOD, mask=P + 0x9000)
+
+
+def scall(**changes):
+    a = dict(SGOOD, **changes)
+    return fa.fa_fwd_sparse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["mask"], a["B"], a["H"], a["Nq"],
+                            a["Nk"], a["d"], a["scale"], a["causal"], a["layout"], a["in_dtype"], a["o_dtype"],
+                            a["stream"])
+
+
+@pytest.mark.parametrize("changes,status", [
+    (dict(mask=0), fa.FA_ERR_INVALID_ARG),
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(in_dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nk=64 * 4096 + 1), fa.FA_ERR_UNSUPPORTED),   # more key blocks than the tile list holds
+])
+def test_fwd_sparse_validation_returns_before_launch(changes, status):
+    assert scall(**changes) == status
+
+
+def test_sparse_granularity_matches_header():
+    t = header_text()
+    assert int(re.search(r"#define FA_SPARSE_BQ (\d+)", t).group(1)) == fa.SPARSE_BQ
+    assert int(re.search(r"#define FA_SPARSE_BK (\d+)", t).group(1)) == fa.SPARSE_BK
