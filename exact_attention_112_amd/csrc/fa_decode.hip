@@ -19,18 +19,19 @@
 // gfx950 design:
 //   * rows of a wave = the grouped query heads of one KV head times the new
 //     tokens (32 per row tile), the MFMA B operand, held in VGPRs;
-//   * a lane owns one key row of a 32-key tile: its K fragments come
-//     straight from the paged cache into the A operand registers of
-//     S^T = K Q^T (v_mfma_f32_32x32x16_bf16), one tile ahead; the same
-//     lane stages the same key row of V into LDS with global_load_lds_dwordx4
-//     (16 bytes a lane, per-lane 64-bit addresses), so one block-table
-//     lookup per lane and tile serves both;
-//   * the V tile is stored chunk-major (the 32 rows of each 16-byte d chunk
-//     contiguous), the order in which one lane's loads of one key row land;
-//     the transposing reads (ds_read_b64_tr_b16) of O^T += V^T P^T then meet
-//     2-way bank conflicts, far below the cache read time of a tile;
+//   * a 32-key tile is read one tile ahead into registers, each load
+//     instruction covering whole key rows (whole 128-byte lines: a lane
+//     owning one key row, as the MFMA operand layout would have it, makes
+//     an instruction touch 32 lines and runs at about half the bandwidth);
+//     a tile starts at a multiple of 32 keys and blocks hold >= 16 keys, so
+//     it spans at most two blocks, whose numbers are read one tile earlier
+//     still, off the path of the tile's own loads;
+//   * at the top of its step the tile goes from registers into LDS, K
+//     swizzled for the 32-row ds_read_b128 of S^T = K Q^T
+//     (v_mfma_f32_32x32x16_bf16), V for the transposing reads
+//     (ds_read_b64_tr_b16) of O^T += V^T P^T;
 //   * the four waves of a workgroup are independent (no barriers), 16 KB of
-//     LDS each (two V stages at d = 128).
+//     LDS each at d = 128 (one K and one V tile).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
@@ -61,15 +62,13 @@ struct DecodeParams {
     float scale_log2;         // scale * log2(e) (tiny positive for scale 0)
 };
 
-// The V tile's LDS slot (16-byte units) of key row `row`, d chunk `c`.
-__device__ __forceinline__ int v_slot(int row, int c) { return c * 32 + row; }
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_decode_split_kernel(DecodeParams p) {
     constexpr int NWV = 4, TK = 32, DCH = D / 8, KK = D / 16, DB = D / 32;
-    constexpr int STAGE = TK * DCH;          // 16-byte slots per V stage
-    constexpr int LPT = DCH / 2;             // V loads per lane per tile
+    constexpr int STAGE = TK * DCH;          // 16-byte slots of one K or V tile
+    constexpr int RPI = 64 / DCH;            // key rows one load instruction covers
+    constexpr int NLD = TK / RPI;            // load instructions per tile and operand
     __shared__ u32x4 smem[NWV * 2 * STAGE];
 
     const int tid = __builtin_amdgcn_workitem_id_x();
@@ -120,58 +119,76 @@ void fa_decode_split_kernel(DecodeParams p) {
     float m = -INFINITY, l0 = 0.f, l1 = 0.f;
     const float sl2 = p.scale_log2;
 
-    lds_char* const vst = (lds_char*)smem + wave * 2 * STAGE * 16;
+    // this wave's LDS: the K tile (row-major, chunks swizzled for the 32-row
+    // ds_read_b128) and the V tile (swizzled for the transposing reads)
+    u32x4* const kst = smem + wave * 2 * STAGE;
+    lds_char* const vst = (lds_char*)(kst + STAGE);
     const int* table = p.block_tables + (long long)b * p.max_blocks;
     const long long head_off = (long long)hk * D;             // elements
     const long long row_stride = (long long)p.Hkv * D;        // elements per token of a block
 
-    // byte address of key `key`'s row (this KV head) in a cache
-    auto key_row = [&](int key) -> long long {
-        const int kc = min(key, k_end - 1);                   // past the chunk: the last key (masked)
-        const int blk = table[kc >> p.bs_log2];
-        const long long tok = ((long long)blk << p.bs_log2) + (kc & ((1 << p.bs_log2) - 1));
-        return (tok * row_stride + head_off) * 2;
+    // Loads: instruction j of a tile reads key rows j*RPI .. j*RPI+RPI-1 whole
+    // (lane: row j*RPI + lrow, chunk lch), so each instruction covers whole
+    // 128-byte lines of the cache; the registers are then written to LDS in
+    // the layouts the MFMA operands are read in.
+    const int lrow = lane / DCH, lch = lane % DCH;
+    // physical blocks of tile i's first and last key: a tile starts at a
+    // multiple of 32 keys and blocks hold >= 16, so it spans at most these two
+    auto tile_blocks = [&](int i, int& ba, int& bb) {
+        const int k0 = k_begin + i * TK;
+        ba = table[k0 >> p.bs_log2];
+        bb = table[min(k0 + TK - 1, k_end - 1) >> p.bs_log2];
     };
-    // tile i: K fragments of this lane's key row into kf; the same row of V
-    // into V stage (i & 1) (chunks 2j + hi, j < LPT)
-    auto load_tile = [&](int i, u32x4 (&kf)[KK]) {
-        const long long off = key_row(k_begin + i * TK + col);
-        const char* kr = (const char*)p.k_cache + off;
-        const char* vr = (const char*)p.v_cache + off;
+    auto load_tile = [&](int i, int ba, int bb, u32x4 (&kr)[NLD], u32x4 (&vr)[NLD]) {
+        const int k0 = k_begin + i * TK;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kf[kk] = *(const u32x4*)(kr + (2 * kk + hi) * 16);
-        lds_char* stg = vst + (i & 1) * STAGE * 16;
-#pragma unroll
-        for (int j = 0; j < LPT; ++j) {
-            // lane (col, hi) of load j writes slot j*64 + lane = (2j + hi)*32 + col:
-            // chunk c = 2j + hi of key row col
-            const int c = 2 * j + hi;
-            __builtin_amdgcn_global_load_lds((const void*)(vr + c * 16), (lds_void*)(stg + j * 1024), 16, 0, 0);
+        for (int j = 0; j < NLD; ++j) {
+            const int key = min(k0 + j * RPI + lrow, k_end - 1);   // past the chunk: its last key (masked)
+            const int blk = (key >> p.bs_log2) == (k0 >> p.bs_log2) ? ba : bb;
+            const long long tok = ((long long)blk << p.bs_log2) + (key & ((1 << p.bs_log2) - 1));
+            const long long off = (tok * row_stride + head_off) * 2 + lch * 16;   // bytes
+            kr[j] = *(const u32x4*)((const char*)p.k_cache + off);
+            vr[j] = *(const u32x4*)((const char*)p.v_cache + off);
         }
     };
 
     const int n_tiles = k_end > k_begin ? (k_end - k_begin + TK - 1) / TK : 0;
-    u32x4 kf[KK], kn[KK];
-    if (n_tiles > 0) load_tile(0, kf);
+    u32x4 kn[NLD], vn[NLD];
+    int ba = 0, bb = 0;
+    if (n_tiles > 0) {
+        tile_blocks(0, ba, bb);
+        load_tile(0, ba, bb, kn, vn);
+        if (n_tiles > 1) tile_blocks(1, ba, bb);
+    }
 
     const int tg = lane >> 4, ti = lane & 15;
     const int tr_row = hi * 4 + (ti >> 2);
     const int tr_dd = 16 * (tg & 1) + 4 * (ti & 3);
 
     for (int i = 0; i < n_tiles; ++i) {
-        // tile i's V is in LDS and its K fragments in kf once every load is back
+        // tile i's rows are in kn/vn and tile i+1's block numbers in ba/bb
+        // once every load is back
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // into LDS (the wave's reads of tile i-1 have all returned: their
+        // data went into tile i-1's MFMAs)
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+            const int r = j * RPI + lrow;
+            kst[r * DCH + k_swz<D>(r, lch)] = kn[j];
+            *(u32x4*)(vst + (r * DCH + v_swz<D>(r, lch)) * 16) = vn[j];
+        }
         if (i + 1 < n_tiles) {
-            // the stage tile i+1 refills was last read by tile i-1, finished
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            load_tile(i + 1, kn);
+            load_tile(i + 1, ba, bb, kn, vn);
+            if (i + 2 < n_tiles) tile_blocks(i + 2, ba, bb);
         }
         const int key0 = k_begin + i * TK;
         f32x16 sc;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[kk]), qreg[kk],
+        for (int kk = 0; kk < KK; ++kk) {
+            const u32x4 kx = kst[col * DCH + k_swz<D>(col, 2 * kk + hi)];
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qreg[kk],
                                                          kk == 0 ? f32x16{} : sc, 0, 0, 0);
+        }
         // keys past the chunk or (causal) after the row's token -> -inf
         const int lim = min(k_end - 1, hi_key) - (key0 + hi * 4);
 #pragma unroll
@@ -203,7 +220,6 @@ void fa_decode_split_kernel(DecodeParams p) {
         }
         // O^T += V^T P^T: slots 0..3 of 16-key group u are keys 16u + hi*4 + 0..3,
         // slots 4..7 keys 16u + 8 + hi*4 + 0..3
-        const lds_char* stg = vst + (i & 1) * STAGE * 16;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const bf16x8 pb = __builtin_bit_cast(bf16x8, (u32x4){pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]});
@@ -213,15 +229,13 @@ void fa_decode_split_kernel(DecodeParams p) {
                 const int dd = db * 32 + tr_dd;
                 const int c = dd >> 3, w = (dd & 7) * 2;
                 const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4*)(stg + v_slot(r0, c) * 16 + w));
+                    (lds_i16x4*)(vst + r0 * (D * 2) + v_swz<D>(r0, c) * 16 + w));
                 const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4*)(stg + v_slot(r1, c) * 16 + w));
+                    (lds_i16x4*)(vst + r1 * (D * 2) + v_swz<D>(r1, c) * 16 + w));
                 const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[db], 0, 0, 0);
             }
         }
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kf[kk] = kn[kk];
     }
 
     // partial result of this chunk: O_s = acc / l (0 if the row saw no key),
