@@ -6,7 +6,7 @@ Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 it shares no code with the GPU path (the only common module is the seeded
 input generator, which holds none of the method's arithmetic).
 
-Four implementations live here (plus the paged-cache and block-sparse
+Five implementations live here (plus the paged-cache and block-sparse
 references in paged.py and sparse.py):
 
 * ``attn_fwd`` -- the plain definition, a two-pass fp64 softmax attention in C
@@ -25,6 +25,9 @@ references in paged.py and sparse.py):
   and a band of visible keys i-left <= j <= i+right ([pwwt] "standard vs
   IO-aware": pre_tokens / next_tokens), plain fp64 C; a row with no visible
   key gives O = 0, LSE = -inf.
+* ``attn_bwd_ex`` -- the gradients of ``attn_fwd_ex``: those of ``attn_bwd``
+  over each row's visible keys, with dK and dV of a KV head summed over the
+  query heads that read it; plain fp64 C.
 * ``online.attn_fwd_online`` -- the pages' own algorithm, the tiled forward
   with the online-softmax recurrence ([nanhubrain] "tiling skeleton",
   [ascendai] section 2.2), in numpy fp64, over caller-chosen block splits.
@@ -89,6 +92,10 @@ class OracleLib:
         x.restype = _c_int
         x.argtypes = ([_c_ptr] * 3 + [_c_i64] * 6 + [_c_int] * 6 + [_c_dbl] + [_c_int] * 3
                       + [_c_ptr, _c_int, _c_ptr, _c_ptr, _c_int])
+        y = self._lib.oracle_attn_bwd_ex
+        y.restype = _c_int
+        y.argtypes = ([_c_ptr] * 4 + [_c_i64] * 6 + [_c_int] * 6 + [_c_dbl] + [_c_int] * 3
+                      + [_c_ptr, _c_int, _c_ptr, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_int])
         self._lib.oracle_max_threads.restype = _c_int
 
     def max_threads(self) -> int:
@@ -229,6 +236,53 @@ class OracleLib:
             raise RuntimeError(f"oracle_attn_fwd_ex failed with code {rc}")
         return o, lse
 
+    def attn_bwd_ex(self, q, k, v, do, *, scale: float, causal: bool = False, window=(-1, -1),
+                    layout: str = "BHND", qrows=None, krows=None, want_dq: bool = True,
+                    want_dkv: bool = True, n_threads: int = 0):
+        """(dQ [B,H,RQ,d], dK [B,Hkv,RK,d], dV [B,Hkv,RK,d]) in float64 with
+        grouped KV heads and a band (as ``attn_fwd_ex``); None for the parts
+        not asked for.  q and do have H heads, k and v Hkv heads; ``qrows`` /
+        ``krows`` as in ``attn_bwd``.
+        """
+        q = np.ascontiguousarray(q, dtype=np.float32)
+        k = np.ascontiguousarray(k, dtype=np.float32)
+        v = np.ascontiguousarray(v, dtype=np.float32)
+        do = np.ascontiguousarray(do, dtype=np.float32)
+        if q.shape != do.shape or k.shape != v.shape:
+            raise ValueError("do must have q's shape and v k's shape")
+        if layout == "BHND":
+            B, H, Nq, d = q.shape
+            Hkv, Nk = k.shape[1], k.shape[2]
+            qs = (H * Nq * d, Nq * d, d)
+            ks = (Hkv * Nk * d, Nk * d, d)
+        elif layout == "BSND":
+            B, Nq, H, d = q.shape
+            Nk, Hkv = k.shape[1], k.shape[2]
+            qs = (Nq * H * d, d, H * d)
+            ks = (Nk * Hkv * d, d, Hkv * d)
+        else:
+            raise ValueError(f"unknown layout {layout!r}")
+
+        def idx(rows, n):
+            if rows is None:
+                return None, None, n
+            a = np.ascontiguousarray(rows, dtype=np.int32)
+            return a, a.ctypes.data, int(a.size)
+
+        qa, qp, RQ = idx(qrows, Nq)
+        ka, kp, RK = idx(krows, Nk)
+        dq = np.empty((B, H, RQ, d), dtype=np.float64) if want_dq else None
+        dk = np.empty((B, Hkv, RK, d), dtype=np.float64) if want_dkv else None
+        dv = np.empty((B, Hkv, RK, d), dtype=np.float64) if want_dkv else None
+        ptr = lambda a: None if a is None else a.ctypes.data
+        rc = self._lib.oracle_attn_bwd_ex(
+            q.ctypes.data, k.ctypes.data, v.ctypes.data, do.ctypes.data,
+            *qs, *ks, B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+            int(window[0]), int(window[1]), qp, RQ, kp, RK, ptr(dq), ptr(dk), ptr(dv), int(n_threads))
+        if rc != 0:
+            raise RuntimeError(f"oracle_attn_bwd_ex failed with code {rc}")
+        return dq, dk, dv
+
     def attn_probs(self, q, k, *, scale: float, causal: bool = False):
         """P [Nq, Nk] (float64) of one head; q [Nq,d], k [Nk,d] float32."""
         q = np.ascontiguousarray(q, dtype=np.float32)
@@ -271,3 +325,7 @@ def attn_bwd(q, k, v, do, **kw):
 
 def attn_fwd_ex(q, k, v, **kw):
     return lib().attn_fwd_ex(q, k, v, **kw)
+
+
+def attn_bwd_ex(q, k, v, do, **kw):
+    return lib().attn_bwd_ex(q, k, v, do, **kw)

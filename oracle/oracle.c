@@ -439,3 +439,201 @@ int oracle_attn_fwd_ex(const float* q, const float* k, const float* v,
     }
     return status;
 }
+
+/* ------------------------------------------------------------------------
+ * Extended backward: the gradients of oracle_attn_bwd under grouped
+ * key/value heads and the band of oracle_attn_fwd_ex, in double.
+ *
+ * Row i of query head h sees keys lo_i..hi_i of key/value head
+ * hk = h / (H / Hkv) (the band and causal flag as in oracle_attn_fwd_ex).
+ * Over that set, P, dP, D_i and dS are those of oracle_attn_bwd.  K and V
+ * of head hk enter the softmax of every query head of its group, so dK_j and
+ * dV_j of head hk are the sums of the per-head terms over those query heads
+ * (the chain rule through the shared rows).  A row with no visible key has
+ * an empty softmax: it has no gradient of its own (dQ_i = 0) and passes none
+ * to any key.
+ * ---------------------------------------------------------------------- */
+
+/* Visible keys [*lo, *hi] of query i; returns 0 when there are none. */
+static int visible_keys(int i, int Nk, int causal, int window_left, int window_right, int* lo, int* hi)
+{
+    int a = 0, z = Nk - 1;
+    if (window_left >= 0 && (int64_t)i - window_left > a) a = i - window_left;
+    if (window_right >= 0 && (int64_t)i + window_right < z) z = i + window_right;
+    if (causal && i < z) z = i;
+    *lo = a;
+    *hi = z;
+    return a <= z;
+}
+
+/* Statistics of one row over keys [lo, hi]: the log-sum-exp of the scaled
+ * scores and D = sum_j P_j (dO . v_j), in double. */
+static void band_grad_stats(const float* qi, const float* gi, const float* kbh, const float* vbh,
+                            int64_t kv_sn, int lo, int hi, int d, double scale,
+                            double* out_lse, double* out_D)
+{
+    double top = -INFINITY;
+    for (int j = lo; j <= hi; ++j) {
+        const float* krow = kbh + (int64_t)j * kv_sn;
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c) dot += (double)qi[c] * (double)krow[c];
+        if (scale * dot > top) top = scale * dot;
+    }
+    double z = 0.0;
+    for (int j = lo; j <= hi; ++j) {
+        const float* krow = kbh + (int64_t)j * kv_sn;
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c) dot += (double)qi[c] * (double)krow[c];
+        z += exp(scale * dot - top);
+    }
+    const double l = top + log(z);
+    double D = 0.0;
+    for (int j = lo; j <= hi; ++j) {
+        const float* krow = kbh + (int64_t)j * kv_sn;
+        const float* vj = vbh + (int64_t)j * kv_sn;
+        double dot = 0.0, dpv = 0.0;
+        for (int c = 0; c < d; ++c) {
+            dot += (double)qi[c] * (double)krow[c];
+            dpv += (double)gi[c] * (double)vj[c];
+        }
+        D += exp(scale * dot - l) * dpv;
+    }
+    *out_lse = l;
+    *out_D = D;
+}
+
+/*
+ * oracle_attn_bwd_ex: dQ [B,H,RQ,d], dK and dV [B,Hkv,RK,d] in double; Q and
+ * dO have H heads (strides q_*), K and V Hkv heads (strides kv_*); rows as in
+ * oracle_attn_bwd.  Only the row statistics that a requested output needs are
+ * computed.  Returns 0, -1 on bad arguments, -2 on allocation failure.
+ */
+int oracle_attn_bwd_ex(const float* q, const float* k, const float* v, const float* dout,
+                       int64_t q_sb, int64_t q_sh, int64_t q_sn,
+                       int64_t kv_sb, int64_t kv_sh, int64_t kv_sn,
+                       int B, int H, int Hkv, int Nq, int Nk, int d,
+                       double scale, int causal, int window_left, int window_right,
+                       const int32_t* qrows, int n_qrows, const int32_t* krows, int n_krows,
+                       double* dq, double* dk, double* dv, int n_threads)
+{
+    if (!q || !k || !v || !dout) return -1;
+    if (B < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 || Nq < 1 || Nk < 1 || d < 1) return -1;
+    const int RQ = qrows ? n_qrows : Nq, RK = krows ? n_krows : Nk;
+    if (RQ < 0 || RK < 0) return -1;
+    for (int r = 0; qrows && r < RQ; ++r)
+        if (qrows[r] < 0 || qrows[r] >= Nq) return -1;
+    for (int r = 0; krows && r < RK; ++r)
+        if (krows[r] < 0 || krows[r] >= Nk) return -1;
+    const int grads_kv = dk != NULL && dv != NULL;
+    if (n_threads <= 0) n_threads = omp_get_max_threads();
+    const int group = H / Hkv;
+
+    /* requested keys as a prefix count over key positions: row i reaches a
+     * requested key iff the count rises within [lo_i, hi_i] */
+    int* kcount = (int*)calloc((size_t)Nk + 1, sizeof(int));
+    double* row_lse = (double*)malloc(sizeof(double) * (size_t)group * Nq);
+    double* row_D = (double*)malloc(sizeof(double) * (size_t)group * Nq);
+    char* need = (char*)malloc((size_t)Nq);
+    if (!kcount || !row_lse || !row_D || !need) {
+        free(kcount); free(row_lse); free(row_D); free(need);
+        return -2;
+    }
+    for (int r = 0; grads_kv && r < RK; ++r) kcount[(krows ? krows[r] : r) + 1] = 1;
+    for (int j = 0; j < Nk; ++j) kcount[j + 1] += kcount[j];
+    for (int i = 0; i < Nq; ++i) {
+        int lo, hi;
+        need[i] = visible_keys(i, Nk, causal, window_left, window_right, &lo, &hi) &&
+                  kcount[hi + 1] - kcount[lo] > 0;
+    }
+    for (int r = 0; dq && r < RQ; ++r) need[qrows ? qrows[r] : r] = 1;
+
+    for (int bk = 0; bk < B * Hkv; ++bk) {
+        const int b = bk / Hkv, hk = bk % Hkv;
+        const int64_t kvoff = (int64_t)b * kv_sb + (int64_t)hk * kv_sh;
+        const float* kbh = k + kvoff;
+        const float* vbh = v + kvoff;
+
+        /* pass 1: statistics of the needed rows of the group's query heads */
+#pragma omp parallel for num_threads(n_threads) schedule(dynamic, 8)
+        for (int64_t t = 0; t < (int64_t)group * Nq; ++t) {
+            const int g = (int)(t / Nq), i = (int)(t % Nq);
+            int lo, hi;
+            row_lse[t] = -INFINITY;
+            row_D[t] = 0.0;
+            if (!need[i] || !visible_keys(i, Nk, causal, window_left, window_right, &lo, &hi)) continue;
+            const int64_t qo = (int64_t)b * q_sb + (int64_t)(hk * group + g) * q_sh + (int64_t)i * q_sn;
+            band_grad_stats(q + qo, dout + qo, kbh, vbh, kv_sn, lo, hi, d, scale, &row_lse[t], &row_D[t]);
+        }
+
+        /* pass 2: dQ of the requested rows of each query head of the group */
+        if (dq) {
+#pragma omp parallel for num_threads(n_threads) schedule(dynamic, 4)
+            for (int64_t t = 0; t < (int64_t)group * RQ; ++t) {
+                const int g = (int)(t / RQ), r = (int)(t % RQ);
+                const int h = hk * group + g;
+                const int i = qrows ? qrows[r] : r;
+                double* out = dq + (((int64_t)b * H + h) * RQ + r) * d;
+                for (int c = 0; c < d; ++c) out[c] = 0.0;
+                int lo, hi;
+                if (!visible_keys(i, Nk, causal, window_left, window_right, &lo, &hi)) continue;
+                const int64_t qo = (int64_t)b * q_sb + (int64_t)h * q_sh + (int64_t)i * q_sn;
+                const float* qi = q + qo;
+                const float* gi = dout + qo;
+                const double l = row_lse[(int64_t)g * Nq + i], Di = row_D[(int64_t)g * Nq + i];
+                for (int j = lo; j <= hi; ++j) {
+                    const float* krow = kbh + (int64_t)j * kv_sn;
+                    const float* vj = vbh + (int64_t)j * kv_sn;
+                    double dot = 0.0, dpv = 0.0;
+                    for (int c = 0; c < d; ++c) {
+                        dot += (double)qi[c] * (double)krow[c];
+                        dpv += (double)gi[c] * (double)vj[c];
+                    }
+                    const double dsij = exp(scale * dot - l) * (dpv - Di);
+                    for (int c = 0; c < d; ++c) out[c] += dsij * (double)krow[c];
+                }
+                for (int c = 0; c < d; ++c) out[c] = scale * out[c];
+            }
+        }
+        if (!grads_kv) continue;
+
+        /* pass 3: dK and dV of the requested keys, summed over the group's
+         * query heads and the queries that see the key */
+#pragma omp parallel for num_threads(n_threads) schedule(dynamic, 4)
+        for (int r = 0; r < RK; ++r) {
+            const int j = krows ? krows[r] : r;
+            const float* krow = kbh + (int64_t)j * kv_sn;
+            const float* vj = vbh + (int64_t)j * kv_sn;
+            double* ok = dk + ((int64_t)bk * RK + r) * d;
+            double* ov = dv + ((int64_t)bk * RK + r) * d;
+            for (int c = 0; c < d; ++c) ok[c] = ov[c] = 0.0;
+            for (int g = 0; g < group; ++g) {
+                const int h = hk * group + g;
+                for (int i = 0; i < Nq; ++i) {
+                    int lo, hi;
+                    if (!visible_keys(i, Nk, causal, window_left, window_right, &lo, &hi) || j < lo || j > hi)
+                        continue;
+                    const int64_t qo = (int64_t)b * q_sb + (int64_t)h * q_sh + (int64_t)i * q_sn;
+                    const float* qi = q + qo;
+                    const float* gi = dout + qo;
+                    double dot = 0.0, dpv = 0.0;
+                    for (int c = 0; c < d; ++c) {
+                        dot += (double)qi[c] * (double)krow[c];
+                        dpv += (double)gi[c] * (double)vj[c];
+                    }
+                    const double pij = exp(scale * dot - row_lse[(int64_t)g * Nq + i]);
+                    const double dsij = pij * (dpv - row_D[(int64_t)g * Nq + i]);
+                    for (int c = 0; c < d; ++c) {
+                        ov[c] += pij * (double)gi[c];
+                        ok[c] += dsij * (double)qi[c];
+                    }
+                }
+            }
+            for (int c = 0; c < d; ++c) ok[c] *= scale;
+        }
+    }
+    free(kcount);
+    free(row_lse);
+    free(row_D);
+    free(need);
+    return 0;
+}
