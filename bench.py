@@ -43,9 +43,11 @@ PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
 
 
 def bwd_algorithmic_bytes(w) -> float:
-    """Read Q, K, V, dO (bf16), O (fp32) and LSE once; write dQ, dK, dV (fp32) once."""
-    per_head = (2 * w.Nq + 2 * w.Nk) * w.d * 2 + w.Nq * w.d * 4 + w.Nq * 4 + (w.Nq + 2 * w.Nk) * w.d * 4
-    return float(per_head) * w.B * w.H
+    """Read Q, K, V, dO (bf16), O (fp32) and LSE once; write dQ, dK, dV (fp32) once
+    (K, V, dK and dV have w.kv_heads heads)."""
+    q_side = w.H * (2 * w.Nq * w.d * 2 + w.Nq * w.d * 4 + w.Nq * 4 + w.Nq * w.d * 4)
+    kv_side = w.kv_heads * (2 * w.Nk * w.d * 2 + 2 * w.Nk * w.d * 4)
+    return float(q_side + kv_side) * w.B
 
 
 def algorithmic_bytes(w, out_bytes: int) -> float:
@@ -142,11 +144,12 @@ def cpu_baseline(w, inp, target_s: float = 10.0):
 
 
 def cpu_baseline_bwd(w, inp, grad, target_s: float = 10.0):
-    """Time the fp64 backward oracle head by head (in (b, h) order) until at
-    least ``target_s`` seconds of work are done: per head, the row statistics
-    of every query plus dQ of every 4th query row and dK, dV of every 4th key
-    row.  The rate counts the algorithmic backward flops of the rows returned
-    (dQ is 2 of the backward's 5 products, dK and dV 3 of them)."""
+    """Time the fp64 backward oracle head by head (in (b, h) order; with grouped
+    KV heads, one KV head's group of query heads at a time) until at least
+    ``target_s`` seconds of work are done: per head, the row statistics of the
+    queries the outputs need plus dQ of every 4th query row and dK, dV of every
+    4th key row.  The rate counts the algorithmic backward flops of the rows
+    returned (dQ is 2 of the backward's 5 products, dK and dV 3 of them)."""
     import numpy as np
     import oracle
 
@@ -154,20 +157,30 @@ def cpu_baseline_bwd(w, inp, grad, target_s: float = 10.0):
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or lib.max_threads()
     qrows = np.arange(0, w.Nq, 4, dtype=np.int32)
     krows = np.arange(0, w.Nk, 4, dtype=np.int32)
-    per_head = 2.5 * 4.0 * w.Nq * w.Nk * w.d * (0.5 if w.causal else 1.0)
+    per_head = 2.5 * w.flops / (w.B * w.H)
     frac = 0.4 * len(qrows) / w.Nq + 0.6 * len(krows) / w.Nk
+    extended = w.kv_heads != w.H or w.window != (-1, -1)
+    group = w.H // w.kv_heads
     done, elapsed = 0, 0.0
     while done < w.B * w.H and elapsed < target_s:
         b, h = divmod(done, w.H)
+        n = group if extended else 1                 # query heads in this call
+        hk = h // group
         if w.layout == "BHND":
-            sl = lambda x: x[b:b + 1, h:h + 1]
+            sq = lambda x: x[b:b + 1, h:h + n]
+            sk = lambda x: x[b:b + 1, hk:hk + 1] if extended else x[b:b + 1, h:h + 1]
         else:
-            sl = lambda x: x[b:b + 1, :, h:h + 1]
+            sq = lambda x: x[b:b + 1, :, h:h + n]
+            sk = lambda x: x[b:b + 1, :, hk:hk + 1] if extended else x[b:b + 1, :, h:h + 1]
         t0 = time.perf_counter()
-        lib.attn_bwd(sl(inp.q), sl(inp.k), sl(inp.v), sl(grad), scale=w.scale, causal=w.causal,
-                     layout=w.layout, qrows=qrows, krows=krows, n_threads=threads)
+        if extended:
+            lib.attn_bwd_ex(sq(inp.q), sk(inp.k), sk(inp.v), sq(grad), scale=w.scale, causal=w.causal,
+                            window=w.window, layout=w.layout, qrows=qrows, krows=krows, n_threads=threads)
+        else:
+            lib.attn_bwd(sq(inp.q), sk(inp.k), sk(inp.v), sq(grad), scale=w.scale, causal=w.causal,
+                         layout=w.layout, qrows=qrows, krows=krows, n_threads=threads)
         elapsed += time.perf_counter() - t0
-        done += 1
+        done += n
     flops = done * per_head * frac
     return {
         "value": flops / elapsed / 1e12,
@@ -175,8 +188,8 @@ def cpu_baseline_bwd(w, inp, grad, target_s: float = 10.0):
         "cores": threads,
         "kind": "oracle",
         "sample": (f"fp64 backward oracle on the first {done} of {w.B * w.H} heads of {w.name}: row "
-                   f"statistics of all {w.Nq} queries, dQ of every 4th query row, dK and dV of every 4th "
-                   f"key row; {flops:.3e} algorithmic flop in {elapsed:.1f} s on {threads} threads"),
+                   f"statistics of the queries the outputs need, dQ of every 4th query row, dK and dV of "
+                   f"every 4th key row; {flops:.3e} algorithmic flop in {elapsed:.1f} s on {threads} threads"),
     }
 
 
@@ -383,9 +396,8 @@ def main(argv=None):
                out=o, lse=lse, window=None if w.window == (-1, -1) else w.window, block_mask=bmask)
 
     if args.which == "bwd":
-        if w.dtype != "bf16" or w.kv_heads != w.H or w.window != (-1, -1):
-            print("bench.py: the backward pass takes bf16 inputs, one KV head per query head and no band",
-                  file=sys.stderr)
+        if w.dtype != "bf16" or w.block_sparse:
+            print("bench.py: the backward pass takes bf16 inputs and no block mask", file=sys.stderr)
             return 2
         grad_vals, grad_bits = I.make_grad(w)
         tdo = up(grad_bits)
@@ -397,7 +409,7 @@ def main(argv=None):
 
         def step():  # noqa: F811  (the timed step of the backward benchmark)
             fa.bwd(tq, tk, tv, o, tdo, lse, causal=w.causal, scale=w.scale, layout=w.layout,
-                   dq=dq, dk=dk, dv=dv, delta=delta)
+                   window=None if w.window == (-1, -1) else w.window, dq=dq, dk=dk, dv=dv, delta=delta)
 
     print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):

@@ -34,7 +34,7 @@ FA_BF16, FA_F32 = 0, 1
 LAYOUTS = {"BHND": FA_BHND, "BSND": FA_BSND}
 
 # the symbols include/fa355.h declares
-EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_sparse", "fa_bwd", "fa_decode", "fa_decode_workspace_bytes", "fa_status_str",
+EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_sparse", "fa_bwd", "fa_bwd_ex", "fa_decode", "fa_decode_workspace_bytes", "fa_status_str",
            "fa_abi_version")
 ABI_VERSION = 1
 
@@ -84,6 +84,9 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float]
                            + [ctypes.c_int] * 4 + [ctypes.c_void_p])
+    lib.fa_bwd_ex.restype = ctypes.c_int
+    lib.fa_bwd_ex.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 + [ctypes.c_float]
+                              + [ctypes.c_int] * 6 + [ctypes.c_void_p])
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_abi_version.restype = ctypes.c_int
@@ -215,15 +218,28 @@ def fa_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int
                              int(causal), int(layout), int(in_dtype), int(o_dtype), stream or None))
 
 
+def fa_bwd_ex(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int, delta: int,
+              B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int, scale: float, causal: int,
+              window_left: int, window_right: int, layout: int, in_dtype: int, o_dtype: int,
+              stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the fa_status."""
+    return int(load().fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Hkv, Nq, Nk, d, float(scale),
+                                int(causal), int(window_left), int(window_right), int(layout), int(in_dtype),
+                                int(o_dtype), stream or None))
+
+
 def bwd(q, k, v, o, do, lse, *, causal: bool = False, scale: float | None = None, layout: str = "BHND",
-        dq=None, dk=None, dv=None, delta=None):
+        window=None, dq=None, dk=None, dv=None, delta=None):
     """Attention backward on torch CUDA tensors (ROCm).
 
     q, k, v, do: bf16, contiguous, in ``layout`` (do has q's shape); o: the
     forward output (float32 or bfloat16, q's shape); lse: float32 [B,H,Nq]
-    from the forward pass.  Returns (dQ, dK, dV), float32 in the layouts of
-    q and k.  ``delta`` (float32 [B,H,Nq]) is the workspace for D_i; it is
-    allocated here when not given.  Enqueued on the current stream.
+    from the forward pass.  k and v may have fewer heads than q (Hkv dividing
+    H: grouped KV heads, as in ``fwd``); ``window`` = (left, right) is the
+    band the forward used (None: no band).  Returns (dQ, dK, dV), float32 in
+    the layouts of q and k (dK, dV with k's heads).  ``delta`` (float32
+    [B,H,Nq]) is the workspace for D_i; it is allocated here when not given.
+    Enqueued on the current stream.
     """
     import torch
 
@@ -246,10 +262,11 @@ def bwd(q, k, v, o, do, lse, *, causal: bool = False, scale: float | None = None
     else:
         B, Nq, H, d = q.shape
         Bk, Nk, Hk, dk_ = k.shape
-    if (Bk, Hk, dk_) != (B, H, d):
+    if (Bk, dk_) != (B, d) or Hk < 1 or H % Hk != 0:
         raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree for layout {layout}")
     if lse.shape != (B, H, Nq) or lse.dtype != torch.float32:
         raise ValueError("lse must be float32 [B,H,Nq]")
+    wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
 
     def out(t, shape, name):
         if t is None:
@@ -265,10 +282,14 @@ def bwd(q, k, v, o, do, lse, *, causal: bool = False, scale: float | None = None
     o_dt = FA_BF16 if o.dtype == torch.bfloat16 else FA_F32
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
-        st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, Nq, Nk, d,
-                    -1.0 if scale is None else float(scale), int(bool(causal)), LAYOUTS[layout],
-                    FA_BF16, o_dt, stream)
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr())
+        sc = -1.0 if scale is None else float(scale)
+        if Hk == H and window is None:
+            st = fa_bwd(*args, B, H, Nq, Nk, d, sc, int(bool(causal)), LAYOUTS[layout], FA_BF16, o_dt, stream)
+        else:
+            st = fa_bwd_ex(*args, B, H, Hk, Nq, Nk, d, sc, int(bool(causal)), wl, wr, LAYOUTS[layout], FA_BF16,
+                           o_dt, stream)
     if st == FA_ERR_INVALID_ARG:
         raise FaInvalidArgument(st, "invalid argument")
     if st == FA_ERR_UNSUPPORTED:

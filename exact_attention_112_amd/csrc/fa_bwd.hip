@@ -54,8 +54,11 @@ struct BwdParams {
     long long q_sb, q_sh, q_sn;   // element strides of Q, O, dO and dQ (batch, head, row)
     long long k_sb, k_sh, k_sn;   // element strides of K, V, dK and dV
     int H, Nq, Nk;
+    int group;                    // query heads per key/value head (H / Hkv)
+    int Hkv;
+    int wl, wr;                   // band: keys i-wl .. i+wr visible (-1: unbounded)
     int n_tiles;                  // row tiles of the kernel's outer loop
-    int BH;                       // B * H
+    int BH;                       // B * H for the delta and dQ kernels, B * Hkv for dK/dV
     float scale;                  // softmax scale (>= 0)
     float scale_log2;             // scale * log2(e); a tiny positive value for scale 0
 };
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(BwdParams p) {
 //   tile against key col;
 //   dK^T, dV^T accumulators: acc[db][r] = d index db*32 + (r/4)*8 + hi*4 + r%4
 //   of key col.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BAND, bool GQA>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
     constexpr int NW = 4, BK = NW * 32, BQ = 32, DCH = D / 8, KK = D / 16, DB = D / 32;
@@ -207,26 +210,45 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     const int col = lane & 31;
     const int hi = lane >> 5;
 
+    // workgroup -> (batch, KV head, key block); the query heads of the KV
+    // head's group all feed this block's dK and dV
     int bh, kt;
     tile_of_block(__builtin_amdgcn_workgroup_id_x(), p.n_tiles, p.BH, CAUSAL, bh, kt);
     if (CAUSAL) kt = p.n_tiles - 1 - kt;   // the longest key blocks (first keys) first
-    const int b = bh / p.H;
-    const int h = bh - b * p.H;
+    const int b = bh / p.Hkv;
+    const int hk = bh - b * p.Hkv;
+    const int h0 = hk * p.group;           // first query head of the group
     const int Nq = p.Nq, Nk = p.Nk;
     const int k0 = kt * BK;               // first key of the workgroup
     const int kw0 = k0 + wave * 32;       // first key of this wave
     const int key = kw0 + col;            // this lane's key
 
-    const long long qoff = (long long)b * p.q_sb + (long long)h * p.q_sh;
-    const long long koff = (long long)b * p.k_sb + (long long)h * p.k_sh;
+    const long long qoff = (long long)b * p.q_sb + (long long)h0 * p.q_sh;
+    const long long koff = (long long)b * p.k_sb + (long long)hk * p.k_sh;
     const char* qbase = (const char*)((const __bf16*)p.q + qoff);
     const char* gbase = (const char*)((const __bf16*)p.dout + qoff);
     const char* vbase = (const char*)((const __bf16*)p.v + koff + (long long)k0 * p.k_sn);
     const unsigned qrb = (unsigned)(p.q_sn * 2), krb = (unsigned)(p.k_sn * 2);
+    const unsigned long long head_bytes = (unsigned long long)p.q_sh * 2;   // next query head
 
-    // query tiles: causal keys >= k0 are seen only by queries >= k0
-    const int q_begin = CAUSAL ? k0 : 0;
-    const int n_qt = q_begin < Nq ? (Nq - q_begin + BQ - 1) / BQ : 0;
+    // queries that see a key of the block [k0, k1]: causal ones are >= k0;
+    // under the band, i + wr >= k0 and i - wl <= k1
+    const int k1 = min(k0 + BK, Nk) - 1;
+    int q_begin = CAUSAL ? k0 : 0;
+    int q_last = Nq - 1;
+    // the same for this wave's keys (a wave past Nk sees no query)
+    int wq_lo = CAUSAL ? kw0 : 0, wq_hi = kw0 < Nk ? Nq - 1 : -1;
+    if constexpr (BAND) {
+        if (p.wr >= 0) {
+            q_begin = max(q_begin, k0 - p.wr);
+            wq_lo = max(wq_lo, kw0 - p.wr);
+        }
+        if (p.wl >= 0) {
+            q_last = min(q_last, k1 + p.wl);
+            wq_hi = min(wq_hi, min(kw0 + 31, Nk - 1) + p.wl);
+        }
+    }
+    const int n_qt = q_begin <= q_last ? (q_last - q_begin) / BQ + 1 : 0;
 
     // K^T fragment (B operand of S = Q K^T): K[key][16kk + 8hi .. +7]
     bf16x8 kreg[KK];
@@ -253,26 +275,25 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     const unsigned long long qaddr = to_sgpr((unsigned long long)qbase);
     const unsigned long long gaddr = to_sgpr((unsigned long long)gbase);
     const int wofs = wave * 1024;   // this wave's part of a stage (bytes)
-#define FA_ISSUE_QG(t)                                                                                           \
+    // step v: Q and dO rows i0 .. of the query head whose rows start at
+    // byte offset hoff (the steps run head-major)
+#define FA_ISSUE_QG(v, hoff, i0)                                                                                 \
     do {                                                                                                         \
-        const int i0_ = q_begin + (t) * BQ;                                                                      \
-        issue_tile<LPWQ, DCH, BQ, NW>(qaddr + (unsigned long long)i0_ * qrb, qrb, ld_q, qst + ((t) & 1) * QTB + wofs, \
-                                      Nq - i0_, wave, lane);                                                     \
-        issue_tile<LPWQ, DCH, BQ, NW>(gaddr + (unsigned long long)i0_ * qrb, qrb, ld_q, gst + ((t) & 1) * QTB + wofs, \
-                                      Nq - i0_, wave, lane);                                                     \
+        const unsigned long long o_ = (hoff) + (unsigned long long)(i0) * qrb;                                   \
+        issue_tile<LPWQ, DCH, BQ, NW>(qaddr + o_, qrb, ld_q, qst + ((v) & 1) * QTB + wofs, Nq - (i0), wave, lane); \
+        issue_tile<LPWQ, DCH, BQ, NW>(gaddr + o_, qrb, ld_q, gst + ((v) & 1) * QTB + wofs, Nq - (i0), wave, lane); \
     } while (0)
 
-    // statistics of a query tile: lse * log2(e) and D (lanes 0..31 of wave 0)
-    const float* lse_bh = p.lse + (long long)bh * Nq;
-    const float* dl_bh = p.delta + (long long)bh * Nq;
+    // statistics of a query tile: lse * log2(e) and D (lanes 0..31 of wave 0),
+    // rows i0 .. of the query head whose statistics start at stat_row
     float st_lse = 0.f, st_dl = 0.f;
-    auto load_stat = [&](int t) {
-        const int i = q_begin + t * BQ + lane;
+    auto load_stat = [&](long long stat_row, int i0) {
+        const int i = i0 + lane;
         st_lse = 0.f;
         st_dl = 0.f;
         if (wave == 0 && lane < BQ && i < Nq) {
-            st_lse = lse_bh[i] * kLog2e;
-            st_dl = dl_bh[i];
+            st_lse = p.lse[stat_row + i] * kLog2e;
+            st_dl = p.delta[stat_row + i];
         }
     };
     auto store_stat = [&](int t) {
@@ -291,23 +312,51 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     const int tr_dd = 16 * (tg & 1) + 4 * (ti & 3);
     const float sl2 = p.scale_log2;
 
+    // steps t = 0 .. n_vt - 1, each issuing the next one's loads; with
+    // grouped heads the query heads of the group run one after the other
+    // (step t: head h0 + t / n_qt, query tile t % n_qt, tracked by counters)
+    const long long stat0 = ((long long)b * p.H + h0) * Nq;
+    const int n_vt = GQA ? n_qt * p.group : n_qt;
+    unsigned long long hoff_nxt = 0;      // the next step's head: Q/dO byte offset,
+    long long stat_nxt = stat0;           // statistics row
+    int i_nxt = q_begin;                  // and first query
     if (n_qt > 0) {
         issue_tile<LPWV, DCH, BK, NW>(to_sgpr((unsigned long long)vbase), krb, ld_v, vblk + wofs, Nk - k0, wave,
                                       lane);
-        FA_ISSUE_QG(0);
-        load_stat(0);
+        FA_ISSUE_QG(0, 0ull, q_begin);
+        load_stat(stat0, q_begin);
     }
-    for (int t = 0; t < n_qt; ++t) {
-        const int i0 = q_begin + t * BQ;
+    for (int t = 0; t < n_vt; ++t) {
+        int i0;
+        if constexpr (GQA) {
+            i0 = i_nxt;
+            i_nxt += BQ;
+            if (i_nxt > q_last) {         // the next step starts the next query head
+                i_nxt = q_begin;
+                hoff_nxt += head_bytes;
+                stat_nxt += Nq;
+            }
+        } else {
+            i0 = q_begin + t * BQ;
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         store_stat(t);
         __syncthreads();
-        if (t + 1 < n_qt) {
-            FA_ISSUE_QG(t + 1);
-            load_stat(t + 1);
+        if (t + 1 < n_vt) {
+            if constexpr (GQA) {
+                FA_ISSUE_QG(t + 1, hoff_nxt, i_nxt);
+                load_stat(stat_nxt, i_nxt);
+            } else {
+                FA_ISSUE_QG(t + 1, 0ull, i0 + BQ);
+                load_stat(stat0, i0 + BQ);
+            }
         }
-        // a wave whose keys all lie after the tile's last query has nothing to add
-        if (CAUSAL && i0 + BQ - 1 < kw0) continue;
+        // a wave none of whose keys this tile's queries see has nothing to add
+        if constexpr (BAND) {
+            if (i0 + BQ - 1 < wq_lo || i0 > wq_hi) continue;
+        } else {
+            if (CAUSAL && i0 + BQ - 1 < kw0) continue;
+        }
 
         const u32x4* qs = (const u32x4*)(qst + (t & 1) * QTB);
         const u32x4* gs = (const u32x4*)(gst + (t & 1) * QTB);
@@ -326,7 +375,9 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             }
         }
         // P = exp2(s*scale*log2e - lse2), dS = P (dP - D); masked pairs get 0
-        const bool masked = (CAUSAL && i0 < kw0 + 31) || i0 + BQ > Nq;
+        bool masked = (CAUSAL && i0 < kw0 + 31) || i0 + BQ > Nq;
+        if constexpr (BAND)
+            masked = masked || (p.wl >= 0 && i0 + BQ - 1 - p.wl > kw0) || (p.wr >= 0 && i0 + p.wr < kw0 + 31);
         unsigned pkp[1][8], pks[1][8];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -340,7 +391,9 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
                 float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][r], sl2, -lv[e]));
                 if (masked) {
                     const int qi = i0 + g * 8 + hi * 4 + e;
-                    const bool vis = qi < Nq && (!CAUSAL || key <= qi);
+                    bool vis = qi < Nq && (!CAUSAL || key <= qi);
+                    if constexpr (BAND)
+                        vis = vis && (p.wl < 0 || key >= qi - p.wl) && (p.wr < 0 || key <= qi + p.wr);
                     pr = vis ? pr : 0.f;
                 }
                 pe[e] = pr;
@@ -369,7 +422,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 //   S^T, dP^T of a 64-key tile: s[kb][r] = key kb*32 + (r/4)*8 + hi*4 + r%4
 //   against query col;  dQ^T accumulator: acc[db][r] = d index
 //   db*32 + (r/4)*8 + hi*4 + r%4 of query col.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BAND>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(BwdParams p) {
     constexpr int NW = 8, BC = 64, BR = NW * 32, DCH = D / 8, KK = D / 16, DB = D / 32;
@@ -395,14 +448,42 @@ void fa_bwd_dq_kernel(BwdParams p) {
     const int q = q_w0 + col;
 
     const long long qoff = (long long)b * p.q_sb + (long long)h * p.q_sh;
-    const long long koff = (long long)b * p.k_sb + (long long)h * p.k_sh;
+    const long long koff = (long long)b * p.k_sb + (long long)(h / p.group) * p.k_sh;
     const unsigned krb = (unsigned)(p.k_sn * 2);
 
-    // key tiles: causal queries see keys <= query only
-    int kv_end = Nk;
-    if (CAUSAL) kv_end = min(Nk, min(q_wg0 + BR, Nq));
-    const int n_kt = (kv_end + BC - 1) / BC;
-    const int n_kt_wave = CAUSAL ? min(n_kt, (q_w0 + 31) / BC + 1) : n_kt;
+    // key tiles t_lo .. t_lo + n_kt - 1 (this wave's: tw_lo .. tw_hi): causal
+    // queries see keys <= query only; under the band, keys i - wl .. i + wr
+    int t_lo = 0, n_kt, tw_lo = 0, tw_hi;
+    // band limits of this lane's query: visible keys lo_key .. hi_key
+    int lo_key = 0, hi_key = 0;
+    const int q_wl = min(q_w0 + 31, Nq - 1);
+    if constexpr (BAND) {
+        const int q_last = min(q_wg0 + BR, Nq) - 1;
+        int key_lo = 0, key_hi = CAUSAL ? min(Nk - 1, q_last) : Nk - 1;
+        // a wave past Nq sees no key
+        int wk_lo = 0, wk_hi = q_w0 < Nq ? (CAUSAL ? min(Nk - 1, q_wl) : Nk - 1) : -1;
+        hi_key = CAUSAL ? min(Nk - 1, q) : Nk - 1;
+        if (p.wl >= 0) {
+            key_lo = max(0, q_wg0 - p.wl);
+            wk_lo = max(0, q_w0 - p.wl);
+            lo_key = q - p.wl;
+        }
+        if (p.wr >= 0) {
+            key_hi = min(key_hi, q_last + p.wr);
+            wk_hi = min(wk_hi, q_wl + p.wr);
+            hi_key = min(hi_key, q + p.wr);
+        }
+        t_lo = key_lo / BC;
+        n_kt = key_lo <= key_hi ? key_hi / BC + 1 - t_lo : 0;
+        tw_lo = wk_lo / BC;
+        tw_hi = wk_lo <= wk_hi ? wk_hi / BC : -1;
+    } else {
+        int kv_end = Nk;
+        if (CAUSAL) kv_end = min(Nk, min(q_wg0 + BR, Nq));
+        n_kt = (kv_end + BC - 1) / BC;
+        tw_hi = (CAUSAL ? min(n_kt, (q_w0 + 31) / BC + 1) : n_kt) - 1;
+    }
+    const int n_kt_wave = tw_hi + 1;      // no band: the wave's tiles are 0 .. n_kt_wave - 1
 
     bf16x8 qreg[KK], greg[KK];
     load_frag<D>(qreg, (const __bf16*)p.q + qoff, p.q_sn, q, Nq, hi);
@@ -430,12 +511,14 @@ void fa_bwd_dq_kernel(BwdParams p) {
     const unsigned long long vaddr = to_sgpr((unsigned long long)((const __bf16*)p.v + koff));
     const unsigned long long tile_bytes = (unsigned long long)BC * krb;
     lds_char* const ldst = lds + wave * 1024;
-#define FA_ISSUE_KV(t)                                                                                           \
+    // step j: key tile t_lo + j (no band: tile j), LDS stage j & 1
+#define FA_ISSUE_KV(j)                                                                                           \
     do {                                                                                                         \
-        issue_tile<LPW, DCH, BC, NW>(kaddr + (unsigned long long)(t) * tile_bytes, krb, ld_k, ldst + ((t) & 1) * TB, \
-                                     Nk - (t) * BC, wave, lane);                                                 \
-        issue_tile<LPW, DCH, BC, NW>(vaddr + (unsigned long long)(t) * tile_bytes, krb, ld_v,                    \
-                                     ldst + (2 + ((t) & 1)) * TB, Nk - (t) * BC, wave, lane);                    \
+        const int t_ = BAND ? t_lo + (j) : (j);                                                                  \
+        issue_tile<LPW, DCH, BC, NW>(kaddr + (unsigned long long)t_ * tile_bytes, krb, ld_k, ldst + ((j) & 1) * TB, \
+                                     Nk - t_ * BC, wave, lane);                                                  \
+        issue_tile<LPW, DCH, BC, NW>(vaddr + (unsigned long long)t_ * tile_bytes, krb, ld_v,                     \
+                                     ldst + (2 + ((j) & 1)) * TB, Nk - t_ * BC, wave, lane);                     \
     } while (0)
 
     const int tg = lane >> 4, ti = lane & 15;
@@ -443,21 +526,29 @@ void fa_bwd_dq_kernel(BwdParams p) {
     const int tr_dd = 16 * (tg & 1) + 4 * (ti & 3);
     const float sl2 = p.scale_log2;
 
-    FA_ISSUE_KV(0);
+    if (!BAND || n_kt > 0) FA_ISSUE_KV(0);
     for (int j = 0; j < n_kt; ++j) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (j + 1 < n_kt) FA_ISSUE_KV(j + 1);
-        if (j >= n_kt_wave) continue;
+        const int tile = BAND ? t_lo + j : j;
+        if constexpr (BAND) {
+            if (tile < tw_lo || tile > tw_hi) continue;
+        } else {
+            if (j >= n_kt_wave) continue;
+        }
 
         const lds_char* ks = lds + (j & 1) * TB;
         const lds_char* vs = lds + (2 + (j & 1)) * TB;
         f32x16 s[2], dp[2];
         rows_times_frag<D, 2, 2>(s, qreg, (const u32x4*)ks, col, hi);
         rows_times_frag<D, 2, 0>(dp, greg, (const u32x4*)vs, col, hi);
-        const int key0 = j * BC;
-        const bool masked = key0 + BC > Nk || (CAUSAL && key0 + BC - 1 > q_w0);
-        const int lim = (CAUSAL ? min(Nk - 1, q) : Nk - 1) - (key0 + hi * 4);
+        const int key0 = tile * BC;
+        bool masked = key0 + BC > Nk || (CAUSAL && key0 + BC - 1 > q_w0);
+        if constexpr (BAND)
+            masked = masked || (p.wl >= 0 && key0 < q_wl - p.wl) || (p.wr >= 0 && key0 + BC - 1 > q_w0 + p.wr);
+        const int lim = (BAND ? hi_key : CAUSAL ? min(Nk - 1, q) : Nk - 1) - (key0 + hi * 4);
+        const int lo_lim = lo_key - (key0 + hi * 4);
         unsigned pk[2][8];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -468,7 +559,10 @@ void fa_bwd_dq_kernel(BwdParams p) {
                 for (int e = 0; e < 2; ++e) {
                     const int r = 2 * jj + e;
                     float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], sl2, -lse2));
-                    if (masked) pr = (kb * 32 + (r >> 2) * 8 + (r & 3)) <= lim ? pr : 0.f;
+                    if (masked) {
+                        const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+                        pr = off <= lim && (!BAND || off >= lo_lim) ? pr : 0.f;
+                    }
                     e2[e] = pr * (dp[kb][r] - dlt);
                 }
                 pk[kb][jj] = pack_bf16x2(e2[0], e2[1]);
@@ -488,8 +582,8 @@ namespace {
 
 bool aligned_b(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
 
-template <int D, bool CAUSAL>
-hipError_t launch_bwd(BwdParams p, bool o_bf16, long long n_rows, hipStream_t s) {
+template <int D, bool CAUSAL, bool BAND>
+hipError_t launch_bwd(BwdParams p, int B, bool o_bf16, long long n_rows, hipStream_t s) {
     // 1. D = rowsum(dO * O)
     const long long rpb = 256 / (D / 8);
     const long long g1 = (n_rows + rpb - 1) / rpb;
@@ -499,30 +593,42 @@ hipError_t launch_bwd(BwdParams p, bool o_bf16, long long n_rows, hipStream_t s)
         hipLaunchKernelGGL((fa_bwd_delta_kernel<D, false>), dim3((unsigned)g1), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // 2. dK, dV (128 keys per workgroup)
+    // 2. dK, dV (128 keys of one KV head per workgroup)
     BwdParams p2 = p;
     p2.n_tiles = (p.Nk + 127) / 128;
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((long long)p2.n_tiles * p.BH)), dim3(256), 0,
-                       s, p2);
+    p2.BH = B * p.Hkv;
+    if (p.group > 1)
+        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, BAND, true>),
+                           dim3((unsigned)((long long)p2.n_tiles * p2.BH)), dim3(256), 0, s, p2);
+    else
+        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, BAND, false>),
+                           dim3((unsigned)((long long)p2.n_tiles * p2.BH)), dim3(256), 0, s, p2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // 3. dQ (256 queries per workgroup)
+    // 3. dQ (256 queries of one query head per workgroup)
     BwdParams p3 = p;
     p3.n_tiles = (p.Nq + 255) / 256;
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((long long)p3.n_tiles * p.BH)), dim3(512), 0, s,
-                       p3);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, BAND>), dim3((unsigned)((long long)p3.n_tiles * p.BH)),
+                       dim3(512), 0, s, p3);
     return hipGetLastError();
 }
 
-}  // namespace
+template <int D>
+hipError_t launch_bwd_d(BwdParams p, int B, bool causal, bool band, bool o_bf16, long long n_rows, hipStream_t s) {
+    if (band) return causal ? launch_bwd<D, true, true>(p, B, o_bf16, n_rows, s)
+                            : launch_bwd<D, false, true>(p, B, o_bf16, n_rows, s);
+    return causal ? launch_bwd<D, true, false>(p, B, o_bf16, n_rows, s)
+                  : launch_bwd<D, false, false>(p, B, o_bf16, n_rows, s);
+}
 
-extern "C" fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                            const float* lse, float* dq, float* dk, float* dv, float* delta,
-                            int B, int H, int Nq, int Nk, int d, float scale, int causal,
-                            int layout, int in_dtype, int o_dtype, void* stream) {
+fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, float* dq, float* dk, float* dv, float* delta,
+                   int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   int window_left, int window_right, int layout, int in_dtype, int o_dtype, void* stream) {
     // ---- validation: no HIP call before it passes
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return FA_ERR_INVALID_ARG;
-    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
     if (layout != FA_BHND && layout != FA_BSND) return FA_ERR_INVALID_ARG;
     if (in_dtype != FA_BF16 && in_dtype != FA_F32) return FA_ERR_INVALID_ARG;
     if (o_dtype != FA_BF16 && o_dtype != FA_F32) return FA_ERR_INVALID_ARG;
@@ -533,16 +639,25 @@ extern "C" fa_status fa_bwd(const void* q, const void* k, const void* v, const v
     if (scale != scale || fabsf(scale) == INFINITY) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (Nq >= (1 << 30) || Nk >= (1 << 30)) return FA_ERR_UNSUPPORTED;
     const long long BH = (long long)B * H;
     const long long n_rows = BH * Nq;
-    if (BH > INT32_MAX || n_rows / 16 > INT32_MAX || BH * ((Nk + 127) / 128) > INT32_MAX ||
+    if (BH > INT32_MAX || n_rows / 16 > INT32_MAX || (long long)B * Hkv * ((Nk + 127) / 128) > INT32_MAX ||
         BH * ((Nq + 255) / 256) > INT32_MAX)
         return FA_ERR_UNSUPPORTED;
     // tiles of up to 128 rows are addressed with 32-bit byte offsets
-    const long long row_bytes = (layout == FA_BSND ? (long long)H * d : (long long)d) * 2;
-    if (128 * row_bytes >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    const long long q_row_bytes = (layout == FA_BSND ? (long long)H * d : (long long)d) * 2;
+    const long long k_row_bytes = (layout == FA_BSND ? (long long)Hkv * d : (long long)d) * 2;
+    if (128 * q_row_bytes >= (1LL << 31) || 128 * k_row_bytes >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
 
     if (scale < 0.f) scale = 1.0f / sqrtf((float)d);
+    // a band edge beyond every key changes nothing: such edges are unbounded
+    // (which also keeps every key index the kernels form within int range)
+    int wl = window_left < 0 ? -1 : window_left;
+    int wr = window_right < 0 ? -1 : window_right;
+    if (wl >= Nq) wl = -1;     // i - wl < 0 <= every key for every query i < Nq
+    if (wr >= Nk) wr = -1;     // i + wr >= Nk - 1 for every query
+    const bool band = wl >= 0 || wr >= 0;
 
     BwdParams p;
     p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
@@ -550,12 +665,16 @@ extern "C" fa_status fa_bwd(const void* q, const void* k, const void* v, const v
     const long long D = d;
     if (layout == FA_BHND) {
         p.q_sb = (long long)H * Nq * D; p.q_sh = (long long)Nq * D; p.q_sn = D;
-        p.k_sb = (long long)H * Nk * D; p.k_sh = (long long)Nk * D; p.k_sn = D;
+        p.k_sb = (long long)Hkv * Nk * D; p.k_sh = (long long)Nk * D; p.k_sn = D;
     } else {
         p.q_sb = (long long)Nq * H * D; p.q_sh = D; p.q_sn = (long long)H * D;
-        p.k_sb = (long long)Nk * H * D; p.k_sh = D; p.k_sn = (long long)H * D;
+        p.k_sb = (long long)Nk * Hkv * D; p.k_sh = D; p.k_sn = (long long)Hkv * D;
     }
     p.H = H; p.Nq = Nq; p.Nk = Nk;
+    p.Hkv = Hkv;
+    p.group = H / Hkv;
+    p.wl = wl;
+    p.wr = wr;
     p.n_tiles = 0;
     p.BH = (int)BH;
     p.scale = scale;
@@ -566,8 +685,26 @@ extern "C" fa_status fa_bwd(const void* q, const void* k, const void* v, const v
 
     hipStream_t s = (hipStream_t)stream;
     const bool c = causal != 0, ob = o_dtype == FA_BF16;
-    hipError_t err;
-    if (d == 128) err = c ? launch_bwd<128, true>(p, ob, n_rows, s) : launch_bwd<128, false>(p, ob, n_rows, s);
-    else err = c ? launch_bwd<64, true>(p, ob, n_rows, s) : launch_bwd<64, false>(p, ob, n_rows, s);
+    const hipError_t err = d == 128 ? launch_bwd_d<128>(p, B, c, band, ob, n_rows, s)
+                                    : launch_bwd_d<64>(p, B, c, band, ob, n_rows, s);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, float* dq, float* dk, float* dv, float* delta,
+                            int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                            int layout, int in_dtype, int o_dtype, void* stream) {
+    return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H, Nq, Nk, d, scale, causal, -1, -1, layout,
+                    in_dtype, o_dtype, stream);
+}
+
+extern "C" fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                               const float* lse, float* dq, float* dk, float* dv, float* delta,
+                               int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                               int window_left, int window_right, int layout, int in_dtype, int o_dtype,
+                               void* stream) {
+    return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Hkv, Nq, Nk, d, scale, causal, window_left,
+                    window_right, layout, in_dtype, o_dtype, stream);
 }

@@ -185,6 +185,36 @@ FA355_API fa_status fa_bwd(const void* q, const void* k, const void* v, const vo
                            int layout, int in_dtype, int o_dtype, void* stream);
 
 /*
+ * fa_bwd_ex -- fa_bwd for grouped key/value heads and a band of visible keys:
+ * the backward pass of fa_fwd_ex.
+ *
+ * The operation: query head h reads key/value head h / (H / Hkv) and row i
+ * sees keys i - window_left .. i + window_right (and j <= i if causal), as in
+ * fa_fwd_ex ([nanhubrain] "GatherPAKVCache" head map, [pwwt] "standard vs
+ * IO-aware" pre_tokens / next_tokens).  The gradients are fa_bwd's over each
+ * row's visible keys; K and V of one head enter the softmax of every query
+ * head of its group, so dK and dV of that head are the sums of the per-head
+ * terms over the group (the chain rule through the shared rows).  A row with
+ * no visible key (forward: O = 0, LSE = -inf) has no gradient: dQ_i = 0, and
+ * it adds nothing to dK or dV.
+ *
+ * Hkv      number of key/value heads, >= 1, dividing H.  k, v, dk and dv have
+ *          Hkv heads in `layout`; q, o, dout, dq and lse have H.
+ * window_left, window_right
+ *          the band, as for fa_fwd_ex (negative = unbounded); lse must come
+ *          from a forward pass with the same band, heads and causal flag.
+ * Every other argument, alignment, ownership, asynchrony and determinism as
+ * for fa_bwd; fa_bwd(...) is fa_bwd_ex(..., Hkv = H, window -1, -1).
+ * FA_ERR_INVALID_ARG also when H % Hkv != 0; FA_ERR_UNSUPPORTED also when
+ * Nq or Nk is 2^30 or more.
+ */
+FA355_API fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, float* dq, float* dk, float* dv, float* delta,
+                              int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                              int window_left, int window_right, int layout, int in_dtype, int o_dtype,
+                              void* stream);
+
+/*
  * fa_decode -- enqueue decode attention over a paged KV cache on `stream`.
  *
  * The operation: Nq new tokens of each of B sequences attend to the

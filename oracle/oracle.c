@@ -467,27 +467,13 @@ static int visible_keys(int i, int Nk, int causal, int window_left, int window_r
 }
 
 /* Statistics of one row over keys [lo, hi]: the log-sum-exp of the scaled
- * scores and D = sum_j P_j (dO . v_j), in double. */
+ * scores and D = sum_j P_j (dO . v_j), in double.  sc and dp are scratch of
+ * Nk doubles (the scaled scores and dO . v_j of the row). */
 static void band_grad_stats(const float* qi, const float* gi, const float* kbh, const float* vbh,
-                            int64_t kv_sn, int lo, int hi, int d, double scale,
+                            int64_t kv_sn, int lo, int hi, int d, double scale, double* sc, double* dp,
                             double* out_lse, double* out_D)
 {
     double top = -INFINITY;
-    for (int j = lo; j <= hi; ++j) {
-        const float* krow = kbh + (int64_t)j * kv_sn;
-        double dot = 0.0;
-        for (int c = 0; c < d; ++c) dot += (double)qi[c] * (double)krow[c];
-        if (scale * dot > top) top = scale * dot;
-    }
-    double z = 0.0;
-    for (int j = lo; j <= hi; ++j) {
-        const float* krow = kbh + (int64_t)j * kv_sn;
-        double dot = 0.0;
-        for (int c = 0; c < d; ++c) dot += (double)qi[c] * (double)krow[c];
-        z += exp(scale * dot - top);
-    }
-    const double l = top + log(z);
-    double D = 0.0;
     for (int j = lo; j <= hi; ++j) {
         const float* krow = kbh + (int64_t)j * kv_sn;
         const float* vj = vbh + (int64_t)j * kv_sn;
@@ -496,8 +482,15 @@ static void band_grad_stats(const float* qi, const float* gi, const float* kbh, 
             dot += (double)qi[c] * (double)krow[c];
             dpv += (double)gi[c] * (double)vj[c];
         }
-        D += exp(scale * dot - l) * dpv;
+        sc[j] = scale * dot;
+        dp[j] = dpv;
+        if (sc[j] > top) top = sc[j];
     }
+    double z = 0.0;
+    for (int j = lo; j <= hi; ++j) z += exp(sc[j] - top);
+    const double l = top + log(z);
+    double D = 0.0;
+    for (int j = lo; j <= hi; ++j) D += exp(sc[j] - l) * dp[j];
     *out_lse = l;
     *out_D = D;
 }
@@ -554,15 +547,31 @@ int oracle_attn_bwd_ex(const float* q, const float* k, const float* v, const flo
         const float* vbh = v + kvoff;
 
         /* pass 1: statistics of the needed rows of the group's query heads */
-#pragma omp parallel for num_threads(n_threads) schedule(dynamic, 8)
-        for (int64_t t = 0; t < (int64_t)group * Nq; ++t) {
-            const int g = (int)(t / Nq), i = (int)(t % Nq);
-            int lo, hi;
-            row_lse[t] = -INFINITY;
-            row_D[t] = 0.0;
-            if (!need[i] || !visible_keys(i, Nk, causal, window_left, window_right, &lo, &hi)) continue;
-            const int64_t qo = (int64_t)b * q_sb + (int64_t)(hk * group + g) * q_sh + (int64_t)i * q_sn;
-            band_grad_stats(q + qo, dout + qo, kbh, vbh, kv_sn, lo, hi, d, scale, &row_lse[t], &row_D[t]);
+        int oom = 0;
+#pragma omp parallel num_threads(n_threads)
+        {
+            double* scratch = (double*)malloc(sizeof(double) * 2 * (size_t)Nk);
+            if (!scratch) {
+#pragma omp atomic write
+                oom = 1;
+            }
+#pragma omp for schedule(dynamic, 8)
+            for (int64_t t = 0; t < (int64_t)group * Nq; ++t) {
+                const int g = (int)(t / Nq), i = (int)(t % Nq);
+                int lo, hi;
+                row_lse[t] = -INFINITY;
+                row_D[t] = 0.0;
+                if (!scratch || !need[i] || !visible_keys(i, Nk, causal, window_left, window_right, &lo, &hi))
+                    continue;
+                const int64_t qo = (int64_t)b * q_sb + (int64_t)(hk * group + g) * q_sh + (int64_t)i * q_sn;
+                band_grad_stats(q + qo, dout + qo, kbh, vbh, kv_sn, lo, hi, d, scale, scratch, scratch + Nk,
+                                &row_lse[t], &row_D[t]);
+            }
+            free(scratch);
+        }
+        if (oom) {
+            free(kcount); free(row_lse); free(row_D); free(need);
+            return -2;
         }
 
         /* pass 2: dQ of the requested rows of each query head of the group */

@@ -155,6 +155,32 @@ def test_bwd_validation_returns_before_launch(changes, status):
     assert bcall(**changes) == status
 
 
+BXGOOD = dict(BGOOD, H=4, Hkv=2, wl=8, wr=-1)
+
+
+def bxcall(**changes):
+    a = dict(BXGOOD, **changes)
+    return fa.fa_bwd_ex(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                        a["delta"], a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+                        a["wl"], a["wr"], a["layout"], a["in_dtype"], a["o_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("changes,status", [
+    (dict(dv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=6, Hkv=4), fa.FA_ERR_INVALID_ARG),      # H not a multiple of Hkv
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(layout=2), fa.FA_ERR_INVALID_ARG),
+    (dict(dq=P + 0x6004), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=math.inf), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(in_dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nq=1 << 30), fa.FA_ERR_UNSUPPORTED),
+])
+def test_bwd_ex_validation_returns_before_launch(changes, status):
+    assert bxcall(**changes) == status
+
+
 def test_bwd_python_wrapper_validates_without_gpu():
     import torch
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)

@@ -13,7 +13,8 @@ MUTANTS = {
     "causal_ignored": ("    if (causal && i < z) z = i;\n", ""),
     "stats_from_wrong_head": ("(int64_t)(hk * group + g) * q_sh + (int64_t)i * q_sn;",
                               "(int64_t)(g * Hkv + hk) * q_sh + (int64_t)i * q_sn;"),
-    "row_term_without_p": ("        D += exp(scale * dot - l) * dpv;\n", "        D += dpv;\n"),
+    "row_term_without_p": ("for (int j = lo; j <= hi; ++j) D += exp(sc[j] - l) * dp[j];",
+                           "for (int j = lo; j <= hi; ++j) D += dp[j];"),
     "lse_without_max": ("    const double l = top + log(z);\n", "    const double l = log(z);\n"),
     "dq_without_scale": ("for (int c = 0; c < d; ++c) out[c] = scale * out[c];", ""),
     "dk_without_scale": ("            for (int c = 0; c < d; ++c) ok[c] *= scale;\n", ""),
