@@ -48,6 +48,8 @@
 #include <stdint.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "fa355.h"
 #include "fa_common.h"
 
@@ -624,6 +626,215 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 
 
 // ---------------------------------------------------------------------------
+// Short-key kernel (bf16, at most 32*NKB <= 128 keys, no band or block mask).
+//
+// With this few keys a query row costs little arithmetic and the pass is
+// bound by HBM: reading Q and writing O.  All of the head's K and V sit in
+// LDS, loaded once per workgroup; the 4 waves of a workgroup then stream
+// query tiles of 32 rows (T each, the waves' tiles side by side), and each
+// row's softmax is taken over all its keys at once (one max, one sum, no
+// rescaling).  A wave's Q tile comes in one tile ahead through direct-to-LDS
+// loads that cover whole rows (two stages per wave, no barriers); its O tile
+// goes out through the stage it has just read, so every store instruction
+// also writes whole rows (whole 128-byte lines).
+// two workgroups of the kernel fit a CU's 160 KB of LDS (else one: one wave per SIMD)
+template <int D, int NKB>
+constexpr int KVB_FITS_TWICE = 2 * (2 * NKB * 32 * D * 2 + 4 * 2 * 32 * D * 2) <= 160 * 1024 ? 1 : 0;
+
+template <int D, int NKB, bool CAUSAL, bool OUT_BF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1 + KVB_FITS_TWICE<D, NKB>)))
+void fa_fwd_short_kernel(FwdParams p, int T, int chunks) {
+    constexpr int NWS = 4, DCH = D / 8, KK = D / 16, DB = D / 32, NK = NKB * 32;
+    constexpr int QTB = 32 * D * 2;              // one Q tile (bytes) = one pass of the O tile
+    constexpr int KVB = NK * D * 2;              // the head's K (or V), rows past Nk zero
+    constexpr int RPI = 64 / DCH;                // rows one load instruction covers
+    constexpr int ES = OUT_BF16 ? 2 : 4;         // bytes per O element
+    constexpr int NPASS = ES / 2;                // O tile passes through one stage
+    constexpr int DP = D / NPASS;                // d values per pass
+    __shared__ __attribute__((aligned(16))) char smem[2 * KVB + NWS * 2 * QTB];
+
+    const int tid = __builtin_amdgcn_workitem_id_x();
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31;
+    const int hi = lane >> 5;
+    const int bid = __builtin_amdgcn_workgroup_id_x();
+    const int bh = bid / chunks;
+    const int chunk = bid - bh * chunks;
+    const int b = bh / p.H;
+    const int h = bh - b * p.H;
+    const int Nq = p.Nq, Nk = p.Nk;
+
+    lds_char* const ks = (lds_char*)smem;
+    lds_char* const vs = ks + KVB;
+    lds_char* const qst = vs + KVB + wave * 2 * QTB;    // this wave's two stages
+
+    // K and V of the KV head into LDS (rows past Nk zero): K swizzled for the
+    // 32-row ds_read_b128, V for the transposing reads
+    {
+        const long long kvoff = (long long)b * p.k_sb + (long long)(h / p.group) * p.k_sh;
+        const __bf16* kg = (const __bf16*)p.k + kvoff;
+        const __bf16* vg = (const __bf16*)p.v + kvoff;
+#pragma unroll
+        for (int e = tid; e < NK * DCH; e += NWS * 64) {
+            const int row = e / DCH, ch = e % DCH;
+            u32x4 kx = (u32x4){0u, 0u, 0u, 0u}, vx = kx;
+            if (row < Nk) {
+                kx = *(const u32x4*)(kg + (long long)row * p.k_sn + ch * 8);
+                vx = *(const u32x4*)(vg + (long long)row * p.k_sn + ch * 8);
+            }
+            *(u32x4*)(ks + (row * DCH + k_swz<D>(row, ch)) * 16) = kx;
+            *(u32x4*)(vs + (row * DCH + v_swz<D>(row, ch)) * 16) = vx;
+        }
+    }
+
+    // this wave's query tiles: rows row0(it) .. +31, it = 0 .. T-1
+    const int wg_row0 = chunk * (T * NWS * 32);
+    auto tile_row0 = [&](int it) { return wg_row0 + (it * NWS + wave) * 32; };
+    const long long qoff = (long long)b * p.q_sb + (long long)h * p.q_sh;
+    const unsigned qrb = (unsigned)(p.q_sn * 2);
+    // Q tile `it` into stage `st`: instruction j, lane l -> row j*RPI + l/DCH,
+    // LDS chunk l%DCH (holding logical chunk (l%DCH) ^ swizzle); rows past Nq
+    // are outside the buffer's range and read as zero
+    auto issue_q = [&](int it, int st) {
+        const int r0 = tile_row0(it);
+        const int nvalid = max(0, min(32, Nq - r0));
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)to_sgpr((unsigned long long)((const __bf16*)p.q + qoff + (long long)min(r0, Nq - 1) * p.q_sn)),
+            (short)0, (int)(nvalid * qrb), 0x00020000);
+#pragma unroll
+        for (int j = 0; j < 32 / RPI; ++j) {
+            const int row = j * RPI + lane / DCH;
+            const int lch = (lane % DCH) ^ (k_swz<D>(row, 0));   // logical chunk landing at LDS chunk lane%DCH
+            load_lds16(rsrc, qst + st * QTB + j * 1024, (unsigned)(row * qrb + lch * 16), 0u);
+        }
+    };
+    if (tile_row0(0) < Nq) issue_q(0, 0);
+    __syncthreads();    // K and V in LDS
+
+    const float sl2 = p.scale_log2;
+    const int tg = lane >> 4, ti = lane & 15;
+    const int tr_row = hi * 4 + (ti >> 2);
+    const int tr_dd = 16 * (tg & 1) + 4 * (ti & 3);
+    const long long o_row_bytes = p.q_sn * ES;
+
+    for (int it = 0; it < T; ++it) {
+        const int r0 = tile_row0(it);
+        if (r0 >= Nq) break;                                   // whole wave
+        const int st = it & 1;
+        lds_char* const stg = qst + st * QTB;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // Q tile `it` landed, earlier stores done
+        bf16x8 qreg[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            qreg[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)(stg + (col * DCH + k_swz<D>(col, 2 * kk + hi)) * 16));
+        // the other stage was last read by the previous tile's O stores
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (it + 1 < T && tile_row0(it + 1) < Nq) issue_q(it + 1, st ^ 1);
+
+        // S^T = K Q^T over all keys
+        f32x16 s[NKB];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const int row = kb * 32 + col;
+                const u32x4 kx = *(const u32x4*)(ks + (row * DCH + k_swz<D>(row, 2 * kk + hi)) * 16);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qreg[kk],
+                                                                kk == 0 ? f32x16{} : s[kb], 0, 0, 0);
+            }
+        // keys past Nk and (causal) after the row's query -> -inf; every row
+        // sees key 0, so its max is finite
+        const int q = r0 + col;
+        const int lim = (CAUSAL ? min(Nk - 1, q) : Nk - 1) - hi * 4;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[kb][r] = (kb * 32 + (r >> 2) * 8 + (r & 3)) <= lim ? s[kb][r] : -INFINITY;
+                mx = fmaxf(mx, s[kb][r]);
+            }
+        const float m2 = pair_max(mx) * sl2;
+        float l0 = 0.f, l1 = 0.f;
+        unsigned pk[NKB][8];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * jj], sl2, -m2));
+                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * jj + 1], sl2, -m2));
+                l0 += e0;
+                l1 += e1;
+                pk[kb][jj] = pack_bf16x2(e0, e1);
+            }
+        const float l_tot = pair_sum(l0 + l1);
+        // O^T = V^T P^T
+        f32x16 oacc[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const bf16x8 pb = __builtin_bit_cast(
+                    bf16x8, (u32x4){pk[kb][4 * u], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]});
+                const int ra = kb * 32 + 16 * u + tr_row, rb = ra + 8;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const int dd = db * 32 + tr_dd;
+                    const int c = dd >> 3, w = (dd & 7) * 2;
+                    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4*)(vs + ra * (D * 2) + v_swz<D>(ra, c) * 16 + w));
+                    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4*)(vs + rb * (D * 2) + v_swz<D>(rb, c) * 16 + w));
+                    const bf16x8 va =
+                        __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[db], 0, 0, 0);
+                }
+            }
+
+        // O = acc / l through the stage just read, NPASS passes of DP d values:
+        // each lane writes its row's pieces (16-byte chunks XOR-swizzled by
+        // row), then each store instruction takes 64/(D/8) whole pass-rows
+        const float inv = 1.0f / l_tot;
+        char* const obase = (char*)p.o + qoff * ES;
+#pragma unroll
+        for (int ps = 0; ps < NPASS; ++ps) {
+            if (ps > 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // previous pass read back
+#pragma unroll
+            for (int db = ps * (DB / NPASS); db < (ps + 1) * (DB / NPASS); ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int dl = db * 32 + g * 8 + hi * 4 - ps * DP;      // first of 4 d values, in the pass
+                    const int byte = dl * ES;
+                    const int phys = (byte >> 4) ^ (col % DCH);
+                    lds_char* dst = stg + col * (DP * ES) + phys * 16 + (byte & 15);
+                    if constexpr (OUT_BF16) {
+                        *(u32x2*)dst = (u32x2){pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                                               pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+                    } else {
+                        *(float4*)dst = make_float4(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
+                                                    oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+                    }
+                }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int j = 0; j < 32 / RPI; ++j) {
+                const int row = j * RPI + lane / DCH, c = lane % DCH;
+                const u32x4 x = *(const u32x4*)(stg + row * (DP * ES) + ((c ^ (row % DCH)) * 16));
+                if (r0 + row < Nq)
+                    *(u32x4*)(obase + (long long)(r0 + row) * o_row_bytes + ps * (DP * ES) + c * 16) = x;
+            }
+        }
+        if (p.lse && hi == 0 && q < Nq)
+            p.lse[(long long)bh * Nq + q] = (m2 + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel: same method, v_mfma_f32_32x32x2f32, P kept in fp32, one
 // 32-key tile per iteration, single-buffered padded LDS.
 template <int D, bool CAUSAL>
@@ -788,6 +999,22 @@ hipError_t launch_bf16(const FwdParams& p, int grid, int mode, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Short-key kernel: NKB = ceil(Nk / 32) blocks of 32 keys.
+#ifndef FA_SHORT_WG_TARGET
+#define FA_SHORT_WG_TARGET 512
+#endif
+constexpr long long kShortWgTarget = FA_SHORT_WG_TARGET;   // workgroups to aim for: one resident round
+template <int D, bool CAUSAL, bool OUT_BF16>
+hipError_t launch_short(const FwdParams& p, int nkb, int grid, int T, int chunks, hipStream_t s) {
+    switch (nkb) {
+    case 1: hipLaunchKernelGGL((fa_fwd_short_kernel<D, 1, CAUSAL, OUT_BF16>), dim3(grid), dim3(256), 0, s, p, T, chunks); break;
+    case 2: hipLaunchKernelGGL((fa_fwd_short_kernel<D, 2, CAUSAL, OUT_BF16>), dim3(grid), dim3(256), 0, s, p, T, chunks); break;
+    case 3: hipLaunchKernelGGL((fa_fwd_short_kernel<D, 3, CAUSAL, OUT_BF16>), dim3(grid), dim3(256), 0, s, p, T, chunks); break;
+    default: hipLaunchKernelGGL((fa_fwd_short_kernel<D, 4, CAUSAL, OUT_BF16>), dim3(grid), dim3(256), 0, s, p, T, chunks); break;
+    }
+    return hipGetLastError();
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_f32(const FwdParams& p, int grid, hipStream_t s) {
     hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), dim3(grid), dim3(kWavesF32 * 64), 0, s, p);
@@ -871,6 +1098,27 @@ fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
     hipStream_t s = (hipStream_t)stream;
     const bool c = causal != 0;
     hipError_t err;
+    // At most 128 keys (bf16, no band, no block mask): the short-key kernel.
+    // Each workgroup streams T tiles of 128 query rows; T is chosen so that
+    // all workgroups are resident at once (two per compute unit, 256 CUs on
+    // MI355X), which measured fastest on the cross-attention workload.
+    const long long q_row_bytes = (layout == FA_BSND ? (long long)H * d : (long long)d) * 2;
+    if (in_dtype == FA_BF16 && mode == kPlain && Nk <= 128 && 32 * q_row_bytes < (1LL << 31)) {
+        const long long n128 = ((long long)Nq + 127) / 128;
+        const long long total = (long long)B * H * n128;
+        const int T = (int)std::max(1LL, std::min(n128, (total + kShortWgTarget - 1) / kShortWgTarget));
+        const long long chunks = (n128 + T - 1) / T;
+        if ((long long)B * H * chunks > INT32_MAX) return FA_ERR_UNSUPPORTED;
+        const int g = (int)((long long)B * H * chunks), nkb = (Nk + 31) / 32, ch = (int)chunks;
+        const bool ob = o_dtype == FA_BF16;
+        if (d == 128)
+            err = c ? (ob ? launch_short<128, true, true>(p, nkb, g, T, ch, s) : launch_short<128, true, false>(p, nkb, g, T, ch, s))
+                    : (ob ? launch_short<128, false, true>(p, nkb, g, T, ch, s) : launch_short<128, false, false>(p, nkb, g, T, ch, s));
+        else
+            err = c ? (ob ? launch_short<64, true, true>(p, nkb, g, T, ch, s) : launch_short<64, true, false>(p, nkb, g, T, ch, s))
+                    : (ob ? launch_short<64, false, true>(p, nkb, g, T, ch, s) : launch_short<64, false, false>(p, nkb, g, T, ch, s));
+        return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+    }
     if (in_dtype == FA_BF16) {
         const bool ob = o_dtype == FA_BF16;
         const int g = (int)grid;
