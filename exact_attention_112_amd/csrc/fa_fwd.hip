@@ -1054,6 +1054,12 @@ fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
     if (scale != scale || fabsf(scale) == INFINITY) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (in_dtype == FA_F32 && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+    // a band edge beyond every key masks nothing: such an edge is unbounded
+    // (the same result; it also keeps every key index the kernels form within
+    // int range)
+    if (Nq >= (1 << 30) || Nk >= (1 << 30)) return FA_ERR_UNSUPPORTED;
+    if (window_left >= Nq) window_left = -1;      // i - wl < 0 for every query i
+    if (window_right >= Nk) window_right = -1;    // i + wr >= Nk - 1 for every query
     const bool band = window_left >= 0 || window_right >= 0;
     // the fp32 kernel serves plain attention only
     if (in_dtype == FA_F32 && (band || Hkv != H || block_mask)) return FA_ERR_UNSUPPORTED;

@@ -66,7 +66,7 @@ typedef enum fa_dtype {
  *          NULL = not written.
  * B, H     batch size and number of heads, >= 1.
  * Nq, Nk   query and key/value sequence lengths, >= 1 (any value: no tile
- *          multiple is required).
+ *          multiple is required); 2^30 or more is FA_ERR_UNSUPPORTED.
  * d        head dimension: 64 or 128 (else FA_ERR_UNSUPPORTED).
  * scale    softmax scale applied to q.k; a negative value selects 1/sqrt(d);
  *          0 is valid (uniform weights); NaN or infinity is FA_ERR_INVALID_ARG.
@@ -106,7 +106,9 @@ FA355_API fa_status fa_fwd(const void* q, const void* k, const void* v, void* o,
  *          that side unbounded.  `causal` still applies (j <= i) on top; a
  *          causal sliding window is (w, -1) with causal = 1, or (w, 0).
  *          Key tiles outside a query tile's band are never loaded.  A row
- *          with no visible key gets O = 0 and LSE = -inf.
+ *          with no visible key gets O = 0 and LSE = -inf.  An edge that
+ *          masks nothing (window_left >= Nq, window_right >= Nk) is taken
+ *          as unbounded.
  * All other arguments, the alignment, ownership and asynchrony rules are
  * those of fa_fwd; fa_fwd(...) is fa_fwd_ex(..., Hkv = H, window -1, -1).
  * FA_ERR_INVALID_ARG also when H % Hkv != 0; FA_ERR_UNSUPPORTED for fp32

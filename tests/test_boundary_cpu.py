@@ -210,6 +210,8 @@ def xcall(**changes):
     (dict(d=80), fa.FA_ERR_UNSUPPORTED),
     (dict(in_dtype=fa.FA_F32, H=2, Hkv=1), fa.FA_ERR_UNSUPPORTED),   # fp32: plain attention only
     (dict(in_dtype=fa.FA_F32, wl=4), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nq=1 << 30), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nk=1 << 30), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_fwd_ex_validation_returns_before_launch(changes, status):
     assert xcall(**changes) == status
