@@ -349,8 +349,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path would shard by heads, see the design notes)", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported "
+              "(heads are independent: the path would shard by heads across GPUs)", file=sys.stderr)
         return 2
 
     import numpy as np

@@ -39,7 +39,7 @@ extern "C" {
 typedef enum fa_status {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad enum, misalignment, NaN/inf scale */
-    FA_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement (e.g. d not 64/128) */
+    FA_ERR_UNSUPPORTED = 2,   /* valid request the library does not implement (e.g. d not 64/128) */
     FA_ERR_HIP = 3            /* the HIP runtime reported an error at launch */
 } fa_status;
 
@@ -167,7 +167,7 @@ FA355_API fa_status fa_fwd_sparse(const void* q, const void* k, const void* v, v
  *           matter; on return it holds D_i in [B, H, Nq] order).
  * B, H, Nq, Nk, d, scale, causal, layout: as for fa_fwd (scale < 0 selects
  *           1/sqrt(d); scale must be the one the forward pass used).
- * in_dtype  FA_BF16 (FA_F32 inputs return FA_ERR_UNSUPPORTED in this build).
+ * in_dtype  FA_BF16 (FA_F32 inputs return FA_ERR_UNSUPPORTED).
  * o_dtype   FA_F32 or FA_BF16.
  * stream    a hipStream_t (NULL = the null stream).
  *
