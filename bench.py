@@ -232,6 +232,46 @@ def cpu_baseline_sparse(w, inp, mask, target_s: float = 10.0):
     }
 
 
+def cpu_baseline_bwd_sparse(w, inp, grad, mask, target_s: float = 10.0):
+    """Time the block-sparse backward oracle (numpy fp64) head by head until
+    ``target_s`` seconds are done: per head, the row statistics of every
+    query plus dQ of every 16th query row and dK, dV of every 16th key row.
+    The rate counts the algorithmic backward flops of the rows returned (2.5 x
+    the forward's per visible pair; dQ is 2 of the 5 products, dK and dV 3)."""
+    import numpy as np
+    from oracle import sparse
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"]
+                      or [1])
+    except Exception:   # noqa: BLE001 (the count is informational)
+        threads = 1
+    qrows = np.arange(0, w.Nq, 16)
+    krows = np.arange(0, w.Nk, 16)
+    bh = (lambda x: x) if w.layout == "BHND" else (lambda x: x.transpose(0, 2, 1, 3))
+    Q, K, V, G = bh(inp.q), bh(inp.k), bh(inp.v), bh(grad)
+    cols = np.minimum(64, w.Nk - 64 * np.arange(mask.shape[3]))
+    done, elapsed, flops = 0, 0.0, 0.0
+    while done < w.B * w.H and elapsed < target_s:
+        b, h = divmod(done, w.H)
+        t0 = time.perf_counter()
+        sparse.attn_bwd_block_sparse(Q[b, h], K[b, h], V[b, h], G[b, h], mask[b, h], bq=256, bk=64,
+                                     scale=w.scale, causal=w.causal, qrows=qrows, krows=krows)
+        elapsed += time.perf_counter() - t0
+        pairs = float((mask[b, h] * cols[None, :]).sum(axis=1) @ np.minimum(256, w.Nq - 256 * np.arange(mask.shape[2])))
+        flops += 2.5 * 4.0 * w.d * pairs * (0.4 * len(qrows) / w.Nq + 0.6 * len(krows) / w.Nk)
+        done += 1
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"numpy fp64 block-sparse backward oracle on the first {done} of {w.B * w.H} heads of "
+                   f"{w.name}: row statistics of every query, dQ of every 16th query row, dK and dV of every "
+                   f"16th key row; {flops:.3e} algorithmic flop in {elapsed:.1f} s"),
+    }
+
+
 def decode_bytes(w, lens) -> float:
     """Algorithmic bytes of one decode call: every cached K and V row of every
     sequence read once (bf16), Q read and O (fp32) and LSE written once, the
@@ -396,8 +436,8 @@ def main(argv=None):
                out=o, lse=lse, window=None if w.window == (-1, -1) else w.window, block_mask=bmask)
 
     if args.which == "bwd":
-        if w.dtype != "bf16" or w.block_sparse:
-            print("bench.py: the backward pass takes bf16 inputs and no block mask", file=sys.stderr)
+        if w.dtype != "bf16":
+            print("bench.py: the backward pass takes bf16 inputs", file=sys.stderr)
             return 2
         grad_vals, grad_bits = I.make_grad(w)
         tdo = up(grad_bits)
@@ -409,7 +449,8 @@ def main(argv=None):
 
         def step():  # noqa: F811  (the timed step of the backward benchmark)
             fa.bwd(tq, tk, tv, o, tdo, lse, causal=w.causal, scale=w.scale, layout=w.layout,
-                   window=None if w.window == (-1, -1) else w.window, dq=dq, dk=dk, dv=dv, delta=delta)
+                   window=None if w.window == (-1, -1) else w.window, block_mask=bmask, dq=dq, dk=dk, dv=dv,
+                   delta=delta)
 
     print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -426,7 +467,8 @@ def main(argv=None):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     bwd = args.which == "bwd"
-    flops = 2.5 * w.flops if bwd else (sparse_flops if w.block_sparse else w.flops)
+    fwd_flops = sparse_flops if w.block_sparse else w.flops
+    flops = 2.5 * fwd_flops if bwd else fwd_flops
     tflops = flops / (ms * 1e-3) / 1e12
     outs = (dq, dk, dv) if bwd else (o, lse)
     if not all(torch.isfinite(t).all() for t in outs):
@@ -436,7 +478,9 @@ def main(argv=None):
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        if bwd:
+        if bwd and w.block_sparse:
+            cpu = cpu_baseline_bwd_sparse(w, inp, grad_vals, mask_np)
+        elif bwd:
             cpu = cpu_baseline_bwd(w, inp, grad_vals)
         elif w.block_sparse:
             cpu = cpu_baseline_sparse(w, inp, mask_np)
@@ -466,7 +510,9 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": ("synthetic (seeded N(0,1) Q/K/V of the workload's shape, seeded BigBird-like block mask)"
+        "data": ("synthetic (seeded N(0,1) Q/K/V/dO of the workload's shape, seeded BigBird-like block mask; "
+                 "O, LSE from the GPU forward)" if w.block_sparse and bwd else
+                 "synthetic (seeded N(0,1) Q/K/V of the workload's shape, seeded BigBird-like block mask)"
                  if w.block_sparse else
                  "synthetic (seeded N(0,1) Q/K/V/dO of the workload's shape; O, LSE from the GPU forward)"
                  if bwd else "synthetic (seeded N(0,1) Q/K/V of the workload's shape)"),

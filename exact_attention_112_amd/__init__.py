@@ -34,7 +34,7 @@ FA_BF16, FA_F32 = 0, 1
 LAYOUTS = {"BHND": FA_BHND, "BSND": FA_BSND}
 
 # the symbols include/fa355.h declares
-EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_sparse", "fa_bwd", "fa_bwd_ex", "fa_decode", "fa_decode_workspace_bytes", "fa_status_str",
+EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_sparse", "fa_bwd", "fa_bwd_ex", "fa_bwd_sparse", "fa_decode", "fa_decode_workspace_bytes", "fa_status_str",
            "fa_abi_version")
 ABI_VERSION = 1
 
@@ -87,6 +87,9 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.fa_bwd_ex.restype = ctypes.c_int
     lib.fa_bwd_ex.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 + [ctypes.c_float]
                               + [ctypes.c_int] * 6 + [ctypes.c_void_p])
+    lib.fa_bwd_sparse.restype = ctypes.c_int
+    lib.fa_bwd_sparse.argtypes = ([ctypes.c_void_p] * 11 + [ctypes.c_int] * 5 + [ctypes.c_float]
+                                  + [ctypes.c_int] * 4 + [ctypes.c_void_p])
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_abi_version.restype = ctypes.c_int
@@ -228,15 +231,25 @@ def fa_bwd_ex(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: 
                                 int(o_dtype), stream or None))
 
 
+def fa_bwd_sparse(q: int, k: int, v: int, o: int, dout: int, lse: int, block_mask: int, dq: int, dk: int,
+                  dv: int, delta: int, B: int, H: int, Nq: int, Nk: int, d: int, scale: float, causal: int,
+                  layout: int, in_dtype: int, o_dtype: int, stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the fa_status."""
+    return int(load().fa_bwd_sparse(q, k, v, o, dout, lse, block_mask, dq, dk, dv, delta, B, H, Nq, Nk, d,
+                                    float(scale), int(causal), int(layout), int(in_dtype), int(o_dtype),
+                                    stream or None))
+
+
 def bwd(q, k, v, o, do, lse, *, causal: bool = False, scale: float | None = None, layout: str = "BHND",
-        window=None, dq=None, dk=None, dv=None, delta=None):
+        window=None, block_mask=None, dq=None, dk=None, dv=None, delta=None):
     """Attention backward on torch CUDA tensors (ROCm).
 
     q, k, v, do: bf16, contiguous, in ``layout`` (do has q's shape); o: the
     forward output (float32 or bfloat16, q's shape); lse: float32 [B,H,Nq]
     from the forward pass.  k and v may have fewer heads than q (Hkv dividing
     H: grouped KV heads, as in ``fwd``); ``window`` = (left, right) is the
-    band the forward used (None: no band).  Returns (dQ, dK, dV), float32 in
+    band the forward used (None: no band); ``block_mask`` the uint8 [B, H,
+    ceil(Nq/256), ceil(Nk/64)] block mask it used (None: dense).  Returns (dQ, dK, dV), float32 in
     the layouts of q and k (dK, dV with k's heads).  ``delta`` (float32
     [B,H,Nq]) is the workspace for D_i; it is allocated here when not given.
     Enqueued on the current stream.
@@ -285,7 +298,17 @@ def bwd(q, k, v, o, do, lse, *, causal: bool = False, scale: float | None = None
         args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr())
         sc = -1.0 if scale is None else float(scale)
-        if Hk == H and window is None:
+        if block_mask is not None:
+            nqb, nkb = (Nq + SPARSE_BQ - 1) // SPARSE_BQ, (Nk + SPARSE_BK - 1) // SPARSE_BK
+            if (block_mask.dtype != torch.uint8 or tuple(block_mask.shape) != (B, H, nqb, nkb)
+                    or not block_mask.is_contiguous() or block_mask.device != q.device):
+                raise ValueError(f"block_mask must be a contiguous uint8 tensor of shape {(B, H, nqb, nkb)} "
+                                 "on q's device")
+            if Hk != H or window is not None:
+                raise ValueError("block_mask does not combine with grouped KV heads or a band")
+            st = fa_bwd_sparse(*args[:6], block_mask.data_ptr(), *args[6:], B, H, Nq, Nk, d, sc,
+                               int(bool(causal)), LAYOUTS[layout], FA_BF16, o_dt, stream)
+        elif Hk == H and window is None:
             st = fa_bwd(*args, B, H, Nq, Nk, d, sc, int(bool(causal)), LAYOUTS[layout], FA_BF16, o_dt, stream)
         else:
             st = fa_bwd_ex(*args, B, H, Hk, Nq, Nk, d, sc, int(bool(causal)), wl, wr, LAYOUTS[layout], FA_BF16,

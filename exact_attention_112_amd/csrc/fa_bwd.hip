@@ -57,11 +57,35 @@ struct BwdParams {
     int group;                    // query heads per key/value head (H / Hkv)
     int Hkv;
     int wl, wr;                   // band: keys i-wl .. i+wr visible (-1: unbounded)
+    const unsigned char* block_mask;  // block-sparse: [B*H][n_qb][n_kb], nonzero = computed
+    int n_qb, n_kb;               // mask blocks: 256 queries x 64 keys
     int n_tiles;                  // row tiles of the kernel's outer loop
     int BH;                       // B * H for the delta and dQ kernels, B * Hkv for dK/dV
     float scale;                  // softmax scale (>= 0)
     float scale_log2;             // scale * log2(e); a tiny positive value for scale 0
 };
+
+// Most 64-key tiles (dQ) or 256-query blocks (dK/dV) a block-sparse call lists.
+constexpr int kMaxSparseList = 4096;
+
+// Sorted list of the indices t < n whose entry row[t] is nonzero, built by
+// one wave (ballot + mbcnt, 64 entries a round) into LDS; returns the count.
+// `extra(t)` is ORed into the stored entry (bits above the index).
+template <typename F>
+__device__ __forceinline__ int build_list(unsigned short* list, int n, int lane, F entry) {
+    int count = 0;
+    for (int base = 0; base < n; base += 64) {
+        const int t = base + lane;
+        const unsigned e = t < n ? entry(t) : 0u;
+        const bool on = e != 0u;
+        const unsigned long long bal = __builtin_amdgcn_ballot_w64(on);
+        const int pos = count + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+        if (on) list[pos] = (unsigned short)((unsigned)t | (e & 0xF000u));
+        count += __builtin_popcountll(bal);
+    }
+    return count;
+}
 
 // Swizzle selector for the LDS tiles: 0 = k_swz (rows read only with
 // ds_read_b128), 2 = kv_swz (rows read both ways).
@@ -191,7 +215,7 @@ __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(BwdParams p) {
 //   tile against key col;
 //   dK^T, dV^T accumulators: acc[db][r] = d index db*32 + (r/4)*8 + hi*4 + r%4
 //   of key col.
-template <int D, bool CAUSAL, bool BAND, bool GQA>
+template <int D, bool CAUSAL, bool BAND, bool GQA, bool SPARSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
     constexpr int NW = 4, BK = NW * 32, BQ = 32, DCH = D / 8, KK = D / 16, DB = D / 32;
@@ -249,6 +273,34 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         }
     }
     const int n_qt = q_begin <= q_last ? (q_last - q_begin) / BQ + 1 : 0;
+    // Block-sparse: the block's 128 keys are two mask columns (waves 0-1 and
+    // 2-3); the steps run over the 32-row tiles of the sorted list of the
+    // 256-query blocks that mark either column (entry: block - first block,
+    // bit 14 + c if column c is marked); a wave skips the blocks that leave
+    // its own column off and sees the others whole (apart from the causal
+    // diagonal and rows past Nq)
+    __shared__ unsigned short qb_list[SPARSE ? kMaxSparseList : 1];
+    __shared__ int qb_len;
+    int n_sp = 0;                          // block-sparse steps
+    const int qb0 = q_begin / 256;
+    if constexpr (SPARSE) {
+        const unsigned char* mk = p.block_mask + (long long)bh * p.n_qb * p.n_kb;
+        const int c0 = kt * 2, c1 = kt * 2 + 1;
+        if (wave == 0) {
+            const int cnt = build_list(qb_list, p.n_qb - qb0, lane, [&](int t) {
+                const unsigned char* mr = mk + (long long)(qb0 + t) * p.n_kb;
+                return (mr[c0] != 0 ? 0x4000u : 0u) | (c1 < p.n_kb && mr[c1] != 0 ? 0x8000u : 0u);
+            });
+            if (lane == 0) qb_len = cnt;
+        }
+        __syncthreads();
+        const int n_list = qb_len;
+        n_sp = 8 * n_list;
+        if (n_list > 0 && qb0 + (qb_list[n_list - 1] & 0xFFF) == p.n_qb - 1)   // the last block may be partial
+            n_sp -= 8 - (Nq - (p.n_qb - 1) * 256 + BQ - 1) / BQ;
+    }
+    // first query of block-sparse step v
+    auto sp_row = [&](int v) { return (qb0 + (qb_list[v >> 3] & 0xFFF)) * 256 + (v & 7) * BQ; };
 
     // K^T fragment (B operand of S = Q K^T): K[key][16kk + 8hi .. +7]
     bf16x8 kreg[KK];
@@ -316,15 +368,16 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     // grouped heads the query heads of the group run one after the other
     // (step t: head h0 + t / n_qt, query tile t % n_qt, tracked by counters)
     const long long stat0 = ((long long)b * p.H + h0) * Nq;
-    const int n_vt = GQA ? n_qt * p.group : n_qt;
+    const int n_vt = SPARSE ? n_sp : GQA ? n_qt * p.group : n_qt;
     unsigned long long hoff_nxt = 0;      // the next step's head: Q/dO byte offset,
     long long stat_nxt = stat0;           // statistics row
     int i_nxt = q_begin;                  // and first query
-    if (n_qt > 0) {
+    if (n_vt > 0) {
+        const int r0 = SPARSE ? sp_row(0) : q_begin;
         issue_tile<LPWV, DCH, BK, NW>(to_sgpr((unsigned long long)vbase), krb, ld_v, vblk + wofs, Nk - k0, wave,
                                       lane);
-        FA_ISSUE_QG(0, 0ull, q_begin);
-        load_stat(stat0, q_begin);
+        FA_ISSUE_QG(0, 0ull, r0);
+        load_stat(stat0, r0);
     }
     for (int t = 0; t < n_vt; ++t) {
         int i0;
@@ -336,6 +389,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
                 hoff_nxt += head_bytes;
                 stat_nxt += Nq;
             }
+        } else if constexpr (SPARSE) {
+            i0 = sp_row(t);
         } else {
             i0 = q_begin + t * BQ;
         }
@@ -346,6 +401,10 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             if constexpr (GQA) {
                 FA_ISSUE_QG(t + 1, hoff_nxt, i_nxt);
                 load_stat(stat_nxt, i_nxt);
+            } else if constexpr (SPARSE) {
+                const int r1 = sp_row(t + 1);
+                FA_ISSUE_QG(t + 1, 0ull, r1);
+                load_stat(stat0, r1);
             } else {
                 FA_ISSUE_QG(t + 1, 0ull, i0 + BQ);
                 load_stat(stat0, i0 + BQ);
@@ -354,6 +413,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         // a wave none of whose keys this tile's queries see has nothing to add
         if constexpr (BAND) {
             if (i0 + BQ - 1 < wq_lo || i0 > wq_hi) continue;
+        } else if constexpr (SPARSE) {
+            if (((qb_list[t >> 3] >> (14 + (wave >> 1))) & 1) == 0 || (CAUSAL && i0 + BQ - 1 < kw0)) continue;
         } else {
             if (CAUSAL && i0 + BQ - 1 < kw0) continue;
         }
@@ -422,7 +483,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 //   S^T, dP^T of a 64-key tile: s[kb][r] = key kb*32 + (r/4)*8 + hi*4 + r%4
 //   against query col;  dQ^T accumulator: acc[db][r] = d index
 //   db*32 + (r/4)*8 + hi*4 + r%4 of query col.
-template <int D, bool CAUSAL, bool BAND>
+template <int D, bool CAUSAL, bool BAND, bool SPARSE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(BwdParams p) {
     constexpr int NW = 8, BC = 64, BR = NW * 32, DCH = D / 8, KK = D / 16, DB = D / 32;
@@ -484,6 +545,20 @@ void fa_bwd_dq_kernel(BwdParams p) {
         tw_hi = (CAUSAL ? min(n_kt, (q_w0 + 31) / BC + 1) : n_kt) - 1;
     }
     const int n_kt_wave = tw_hi + 1;      // no band: the wave's tiles are 0 .. n_kt_wave - 1
+    // Block-sparse: the workgroup's 256 queries are one mask row; the steps
+    // run over the sorted list of the key tiles it marks (a marked tile is
+    // seen whole, apart from the causal diagonal and the ragged last tile)
+    __shared__ unsigned short tile_list[SPARSE ? kMaxSparseList : 1];
+    __shared__ int list_len;
+    if constexpr (SPARSE) {
+        const unsigned char* mrow = p.block_mask + ((long long)bh * p.n_qb + qt) * p.n_kb;
+        if (wave == 0) {
+            const int cnt = build_list(tile_list, n_kt, lane, [&](int t) { return mrow[t] != 0 ? 1u : 0u; });
+            if (lane == 0) list_len = cnt;
+        }
+        __syncthreads();
+        n_kt = list_len;
+    }
 
     bf16x8 qreg[KK], greg[KK];
     load_frag<D>(qreg, (const __bf16*)p.q + qoff, p.q_sn, q, Nq, hi);
@@ -511,10 +586,12 @@ void fa_bwd_dq_kernel(BwdParams p) {
     const unsigned long long vaddr = to_sgpr((unsigned long long)((const __bf16*)p.v + koff));
     const unsigned long long tile_bytes = (unsigned long long)BC * krb;
     lds_char* const ldst = lds + wave * 1024;
-    // step j: key tile t_lo + j (no band: tile j), LDS stage j & 1
+    // step j: key tile t_lo + j (no band: tile j; block-sparse: list entry j),
+    // LDS stage j & 1
+#define FA_STEP_TILE(j) (SPARSE ? (int)tile_list[(j)] : BAND ? t_lo + (j) : (j))
 #define FA_ISSUE_KV(j)                                                                                           \
     do {                                                                                                         \
-        const int t_ = BAND ? t_lo + (j) : (j);                                                                  \
+        const int t_ = FA_STEP_TILE(j);                                                                          \
         issue_tile<LPW, DCH, BC, NW>(kaddr + (unsigned long long)t_ * tile_bytes, krb, ld_k, ldst + ((j) & 1) * TB, \
                                      Nk - t_ * BC, wave, lane);                                                  \
         issue_tile<LPW, DCH, BC, NW>(vaddr + (unsigned long long)t_ * tile_bytes, krb, ld_v,                     \
@@ -526,14 +603,16 @@ void fa_bwd_dq_kernel(BwdParams p) {
     const int tr_dd = 16 * (tg & 1) + 4 * (ti & 3);
     const float sl2 = p.scale_log2;
 
-    if (!BAND || n_kt > 0) FA_ISSUE_KV(0);
+    if ((!BAND && !SPARSE) || n_kt > 0) FA_ISSUE_KV(0);
     for (int j = 0; j < n_kt; ++j) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (j + 1 < n_kt) FA_ISSUE_KV(j + 1);
-        const int tile = BAND ? t_lo + j : j;
+        const int tile = FA_STEP_TILE(j);
         if constexpr (BAND) {
             if (tile < tw_lo || tile > tw_hi) continue;
+        } else if constexpr (SPARSE) {
+            if (tile > tw_hi) continue;
         } else {
             if (j >= n_kt_wave) continue;
         }
@@ -570,6 +649,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
         tr_times_packed<D, 2>(acc, pk, ks, tr_row, tr_dd);
     }
 #undef FA_ISSUE_KV
+#undef FA_STEP_TILE
 
     if (q < Nq) store_rows_f32<D>(p.dq + qoff + (long long)q * p.q_sn, acc, p.scale, hi);
 }
@@ -582,7 +662,7 @@ namespace {
 
 bool aligned_b(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
 
-template <int D, bool CAUSAL, bool BAND>
+template <int D, bool CAUSAL, bool BAND, bool SPARSE>
 hipError_t launch_bwd(BwdParams p, int B, bool o_bf16, long long n_rows, hipStream_t s) {
     // 1. D = rowsum(dO * O)
     const long long rpb = 256 / (D / 8);
@@ -597,32 +677,35 @@ hipError_t launch_bwd(BwdParams p, int B, bool o_bf16, long long n_rows, hipStre
     BwdParams p2 = p;
     p2.n_tiles = (p.Nk + 127) / 128;
     p2.BH = B * p.Hkv;
-    if (p.group > 1)
-        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, BAND, true>),
+    if (!SPARSE && p.group > 1)
+        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, BAND, true, false>),
                            dim3((unsigned)((long long)p2.n_tiles * p2.BH)), dim3(256), 0, s, p2);
     else
-        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, BAND, false>),
+        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, BAND, false, SPARSE>),
                            dim3((unsigned)((long long)p2.n_tiles * p2.BH)), dim3(256), 0, s, p2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // 3. dQ (256 queries of one query head per workgroup)
     BwdParams p3 = p;
     p3.n_tiles = (p.Nq + 255) / 256;
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, BAND>), dim3((unsigned)((long long)p3.n_tiles * p.BH)),
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, BAND, SPARSE>), dim3((unsigned)((long long)p3.n_tiles * p.BH)),
                        dim3(512), 0, s, p3);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_bwd_d(BwdParams p, int B, bool causal, bool band, bool o_bf16, long long n_rows, hipStream_t s) {
-    if (band) return causal ? launch_bwd<D, true, true>(p, B, o_bf16, n_rows, s)
-                            : launch_bwd<D, false, true>(p, B, o_bf16, n_rows, s);
-    return causal ? launch_bwd<D, true, false>(p, B, o_bf16, n_rows, s)
-                  : launch_bwd<D, false, false>(p, B, o_bf16, n_rows, s);
+hipError_t launch_bwd_d(BwdParams p, int B, bool causal, bool band, bool sparse, bool o_bf16, long long n_rows,
+                        hipStream_t s) {
+    if (sparse) return causal ? launch_bwd<D, true, false, true>(p, B, o_bf16, n_rows, s)
+                              : launch_bwd<D, false, false, true>(p, B, o_bf16, n_rows, s);
+    if (band) return causal ? launch_bwd<D, true, true, false>(p, B, o_bf16, n_rows, s)
+                            : launch_bwd<D, false, true, false>(p, B, o_bf16, n_rows, s);
+    return causal ? launch_bwd<D, true, false, false>(p, B, o_bf16, n_rows, s)
+                  : launch_bwd<D, false, false, false>(p, B, o_bf16, n_rows, s);
 }
 
 fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                   const float* lse, float* dq, float* dk, float* dv, float* delta,
+                   const float* lse, const unsigned char* block_mask, float* dq, float* dk, float* dv, float* delta,
                    int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                    int window_left, int window_right, int layout, int in_dtype, int o_dtype, void* stream) {
     // ---- validation: no HIP call before it passes
@@ -658,6 +741,10 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
     if (wl >= Nq) wl = -1;     // i - wl < 0 <= every key for every query i < Nq
     if (wr >= Nk) wr = -1;     // i + wr >= Nk - 1 for every query
     const bool band = wl >= 0 || wr >= 0;
+    // block-sparse: no band, no grouped heads, mask lists within kMaxSparseList
+    const bool sparse = block_mask != nullptr;
+    if (sparse && (band || Hkv != H || (Nk + 63) / 64 > kMaxSparseList || (Nq + 255) / 256 > kMaxSparseList))
+        return FA_ERR_UNSUPPORTED;
 
     BwdParams p;
     p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
@@ -675,6 +762,9 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
     p.group = H / Hkv;
     p.wl = wl;
     p.wr = wr;
+    p.block_mask = block_mask;
+    p.n_qb = (Nq + 255) / 256;       // mask rows: 256 queries
+    p.n_kb = (Nk + 63) / 64;         // mask columns: 64 keys
     p.n_tiles = 0;
     p.BH = (int)BH;
     p.scale = scale;
@@ -685,8 +775,8 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
 
     hipStream_t s = (hipStream_t)stream;
     const bool c = causal != 0, ob = o_dtype == FA_BF16;
-    const hipError_t err = d == 128 ? launch_bwd_d<128>(p, B, c, band, ob, n_rows, s)
-                                    : launch_bwd_d<64>(p, B, c, band, ob, n_rows, s);
+    const hipError_t err = d == 128 ? launch_bwd_d<128>(p, B, c, band, sparse, ob, n_rows, s)
+                                    : launch_bwd_d<64>(p, B, c, band, sparse, ob, n_rows, s);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -696,8 +786,8 @@ extern "C" fa_status fa_bwd(const void* q, const void* k, const void* v, const v
                             const float* lse, float* dq, float* dk, float* dv, float* delta,
                             int B, int H, int Nq, int Nk, int d, float scale, int causal,
                             int layout, int in_dtype, int o_dtype, void* stream) {
-    return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H, Nq, Nk, d, scale, causal, -1, -1, layout,
-                    in_dtype, o_dtype, stream);
+    return bwd_impl(q, k, v, o, dout, lse, nullptr, dq, dk, dv, delta, B, H, H, Nq, Nk, d, scale, causal, -1, -1,
+                    layout, in_dtype, o_dtype, stream);
 }
 
 extern "C" fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -705,6 +795,15 @@ extern "C" fa_status fa_bwd_ex(const void* q, const void* k, const void* v, cons
                                int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                                int window_left, int window_right, int layout, int in_dtype, int o_dtype,
                                void* stream) {
-    return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Hkv, Nq, Nk, d, scale, causal, window_left,
-                    window_right, layout, in_dtype, o_dtype, stream);
+    return bwd_impl(q, k, v, o, dout, lse, nullptr, dq, dk, dv, delta, B, H, Hkv, Nq, Nk, d, scale, causal,
+                    window_left, window_right, layout, in_dtype, o_dtype, stream);
+}
+
+extern "C" fa_status fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                   const float* lse, const unsigned char* block_mask, float* dq, float* dk,
+                                   float* dv, float* delta, int B, int H, int Nq, int Nk, int d, float scale,
+                                   int causal, int layout, int in_dtype, int o_dtype, void* stream) {
+    if (!block_mask) return FA_ERR_INVALID_ARG;
+    return bwd_impl(q, k, v, o, dout, lse, block_mask, dq, dk, dv, delta, B, H, H, Nq, Nk, d, scale, causal, -1,
+                    -1, layout, in_dtype, o_dtype, stream);
 }

@@ -217,6 +217,31 @@ FA355_API fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const
                               void* stream);
 
 /*
+ * fa_bwd_sparse -- fa_bwd for block-sparse attention: the backward pass of
+ * fa_fwd_sparse.
+ *
+ * The operation: key j is visible to query i iff
+ * block_mask[b][h][i / FA_SPARSE_BQ][j / FA_SPARSE_BK] != 0 (and j <= i if
+ * causal), as in fa_fwd_sparse ([nanhubrain] "SparseFlashAttention": the
+ * blocks the mask leaves off are skipped).  The gradients are fa_bwd's over
+ * each row's visible keys; a row with no visible key has no gradient and
+ * adds nothing to dK or dV.  Key blocks the mask leaves off are never read
+ * for dQ, and query blocks that leave a key block off are never read for its
+ * dK and dV.
+ *
+ * block_mask  device pointer, uint8 [B, H, ceil(Nq/256), ceil(Nk/64)]
+ *             contiguous, the mask the forward pass used.
+ * Every other argument, alignment, ownership, asynchrony and determinism as
+ * for fa_bwd.  FA_ERR_INVALID_ARG also for a NULL mask; FA_ERR_UNSUPPORTED
+ * also for more than 4096 key blocks or more than 4096 query blocks, or Nq or
+ * Nk of 2^30 or more.
+ */
+FA355_API fa_status fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                  const float* lse, const unsigned char* block_mask, float* dq, float* dk, float* dv,
+                                  float* delta, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                                  int layout, int in_dtype, int o_dtype, void* stream);
+
+/*
  * fa_decode -- enqueue decode attention over a paged KV cache on `stream`.
  *
  * The operation: Nq new tokens of each of B sequences attend to the

@@ -70,3 +70,48 @@ def tol_for(w: I.Workload, out_dtype=None):
     if w.dtype == "f32":
         return F32_TOL
     return BF16_OUT_TOL if out_dtype == torch.bfloat16 else BF16_TOL
+
+
+def bwd_bounds(q, k, v, do, o_ref, lse_ref, o_given, lse_given, scale, visible, qrows, krows):
+    """Elementwise error bounds of the backward pass for one head (the bound
+    tests/test_gpu_bwd.py derives: P and dS rounded to bf16, u = 2^-8, fp32
+    sums eps = 1e-5, and the exact effect of the O and LSE the backward is
+    given), over the pairs visible(rows, cols) marks.  q, do, o_* [Nq, d];
+    k, v [Nk, d]; lse_* [Nq] (float64).  Returns (bq [RQ,d], bk [RK,d],
+    bv [RK,d])."""
+    u, eps = 2.0 ** -8, 1e-5
+    Nq, Nk = q.shape[0], k.shape[0]
+    live = np.isfinite(lse_ref)
+    lse = np.where(live, lse_ref, 0.0)
+    D = np.sum(do * o_ref, axis=1)
+    Dabs = np.sum(np.abs(do * o_ref), axis=1)
+    dD = np.abs(np.sum(do * (o_given - o_ref), axis=1))
+    dL = np.where(live, np.expm1(np.abs(np.where(live, lse_given, 0.0) - lse) + 1e-7 * np.abs(lse)), 0.0)
+
+    def ds_err(rows_q, cols_k):
+        s = scale * (q[rows_q] @ k[cols_k].T)
+        p = np.where(visible(rows_q, cols_k), np.exp(np.minimum(s - lse[rows_q, None], 80.0)), 0.0)
+        dp = do[rows_q] @ v[cols_k].T
+        dp_abs = np.abs(do[rows_q]) @ np.abs(v[cols_k]).T
+        ds = p * (dp - D[rows_q, None])
+        e = (u + dL[rows_q, None]) * np.abs(ds) + p * (eps * (dp_abs + Dabs[rows_q, None]) + dD[rows_q, None])
+        return e, p
+
+    allq, allk = np.arange(Nq), np.arange(Nk)
+    eq, _ = ds_err(np.asarray(qrows), allk)
+    bq = scale * (eq @ np.abs(k))
+    ek, pk = ds_err(allq, np.asarray(krows))
+    bk = scale * (ek.T @ np.abs(q))
+    bv = (pk * (u + eps + dL[:, None])).T @ np.abs(do)
+    return bq, bk, bv
+
+
+def check_bound(name, got, ref, bound):
+    """|got - ref| <= 1.1 x bound + 1e-5 x max|ref| elementwise, and finite."""
+    err = np.abs(got - ref)
+    slack = 1e-5 * max(1e-30, float(np.max(np.abs(ref))))
+    ratio = float(np.max(err / (1.1 * bound + slack)))
+    rel = float(np.max(err) / max(1e-30, np.max(np.abs(ref))))
+    log(f"    {name}: max|err| {np.max(err):.3e} (rel {rel:.2e})  max err/bound {ratio:.3f}")
+    assert np.isfinite(got).all(), f"{name}: non-finite"
+    assert ratio <= 1.0, f"{name}: error exceeds its bound (ratio {ratio:.3f})"
