@@ -181,6 +181,26 @@ def test_bwd_ex_validation_returns_before_launch(changes, status):
     assert bxcall(**changes) == status
 
 
+def bscall(**changes):
+    a = dict(BGOOD, mask=P + 0xa000, **changes)
+    return fa.fa_bwd_sparse(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["mask"], a["dq"], a["dk"],
+                            a["dv"], a["delta"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+                            a["layout"], a["in_dtype"], a["o_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("changes,status", [
+    (dict(mask=0), fa.FA_ERR_INVALID_ARG),           # the mask is required
+    (dict(dq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=P + 0x4002), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nk=64 * 4096 + 1), fa.FA_ERR_UNSUPPORTED),   # more key blocks than a list holds
+    (dict(Nq=256 * 4096 + 1), fa.FA_ERR_UNSUPPORTED),  # more query blocks than a list holds
+])
+def test_bwd_sparse_validation_returns_before_launch(changes, status):
+    assert bscall(**changes) == status
+
+
 def test_bwd_python_wrapper_validates_without_gpu():
     import torch
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
