@@ -182,7 +182,7 @@ def test_bwd_ex_validation_returns_before_launch(changes, status):
 
 
 def bscall(**changes):
-    a = dict(BGOOD, mask=P + 0xa000, **changes)
+    a = dict(dict(BGOOD, mask=P + 0xa000), **changes)
     return fa.fa_bwd_sparse(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["mask"], a["dq"], a["dk"],
                             a["dv"], a["delta"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
                             a["layout"], a["in_dtype"], a["o_dtype"], a["stream"])
