@@ -236,9 +236,13 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 
     // workgroup -> (batch, KV head, key block); the query heads of the KV
     // head's group all feed this block's dK and dV
+    // causal and block-sparse: the key blocks in ascending order, heads fastest,
+    // so the blocks that most queries see (the first keys under the causal
+    // mask; global columns at the start of a block-sparse mask) start first
+    // and no long block is left for the end of the grid
     int bh, kt;
-    tile_of_block(__builtin_amdgcn_workgroup_id_x(), p.n_tiles, p.BH, CAUSAL, bh, kt);
-    if (CAUSAL) kt = p.n_tiles - 1 - kt;   // the longest key blocks (first keys) first
+    tile_of_block(__builtin_amdgcn_workgroup_id_x(), p.n_tiles, p.BH, CAUSAL || SPARSE, bh, kt);
+    if (CAUSAL || SPARSE) kt = p.n_tiles - 1 - kt;
     const int b = bh / p.Hkv;
     const int hk = bh - b * p.Hkv;
     const int h0 = hk * p.group;           // first query head of the group
