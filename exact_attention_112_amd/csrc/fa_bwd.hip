@@ -341,11 +341,14 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     } while (0)
 
     // statistics of a query tile: lse * log2(e) and D (lanes 0..31 of wave 0),
-    // rows i0 .. of the query head whose statistics start at stat_row
+    // rows i0 .. of the query head whose statistics start at stat_row.  Rows
+    // past Nq (their Q and dO are copies of row Nq-1, finite) take lse = +inf
+    // and D = 0, so their P is exactly 0, and so is their dS: they add nothing
+    // and need no mask.
     float st_lse = 0.f, st_dl = 0.f;
     auto load_stat = [&](long long stat_row, int i0) {
         const int i = i0 + lane;
-        st_lse = 0.f;
+        st_lse = INFINITY;
         st_dl = 0.f;
         if (wave == 0 && lane < BQ && i < Nq) {
             st_lse = p.lse[stat_row + i] * kLog2e;
@@ -440,7 +443,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             }
         }
         // P = exp2(s*scale*log2e - lse2), dS = P (dP - D); masked pairs get 0
-        bool masked = (CAUSAL && i0 < kw0 + 31) || i0 + BQ > Nq;
+        // (rows past Nq have P = 0 from their statistics)
+        bool masked = CAUSAL && i0 < kw0 + 31;
         if constexpr (BAND)
             masked = masked || (p.wl >= 0 && i0 + BQ - 1 - p.wl > kw0) || (p.wr >= 0 && i0 + p.wr < kw0 + 31);
         unsigned pkp[1][8], pks[1][8];
@@ -456,7 +460,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
                 float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][r], sl2, -lv[e]));
                 if (masked) {
                     const int qi = i0 + g * 8 + hi * 4 + e;
-                    bool vis = qi < Nq && (!CAUSAL || key <= qi);
+                    bool vis = !CAUSAL || key <= qi;
                     if constexpr (BAND)
                         vis = vis && (p.wl < 0 || key >= qi - p.wl) && (p.wr < 0 || key <= qi + p.wr);
                     pr = vis ? pr : 0.f;
@@ -632,24 +636,27 @@ void fa_bwd_dq_kernel(BwdParams p) {
             masked = masked || (p.wl >= 0 && key0 < q_wl - p.wl) || (p.wr >= 0 && key0 + BC - 1 > q_w0 + p.wr);
         const int lim = (BAND ? hi_key : CAUSAL ? min(Nk - 1, q) : Nk - 1) - (key0 + hi * 4);
         const int lo_lim = lo_key - (key0 + hi * 4);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], sl2, -lse2));
+        // the per-element mask only on tiles that need it (a uniform branch)
+        if (masked) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+                    s[kb][r] = off <= lim && (!BAND || off >= lo_lim) ? s[kb][r] : 0.f;
+                }
+        }
         unsigned pk[2][8];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                float e2[2];
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int r = 2 * jj + e;
-                    float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], sl2, -lse2));
-                    if (masked) {
-                        const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
-                        pr = off <= lim && (!BAND || off >= lo_lim) ? pr : 0.f;
-                    }
-                    e2[e] = pr * (dp[kb][r] - dlt);
-                }
-                pk[kb][jj] = pack_bf16x2(e2[0], e2[1]);
-            }
+            for (int jj = 0; jj < 8; ++jj)
+                pk[kb][jj] = pack_bf16x2(s[kb][2 * jj] * (dp[kb][2 * jj] - dlt),
+                                         s[kb][2 * jj + 1] * (dp[kb][2 * jj + 1] - dlt));
         tr_times_packed<D, 2>(acc, pk, ks, tr_row, tr_dd);
     }
 #undef FA_ISSUE_KV
