@@ -448,30 +448,61 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         if constexpr (BAND)
             masked = masked || (p.wl >= 0 && i0 + BQ - 1 - p.wl > kw0) || (p.wr >= 0 && i0 + p.wr < kw0 + 31);
         unsigned pkp[1][8], pks[1][8];
+        if constexpr (BAND) {
+            // the band's edges: the per-element mask only on the tiles that need
+            // it, in a uniform branch
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float4 l4 = *(const float4*)&stat[t & 1][0][g * 8 + hi * 4];
-            const float4 d4 = *(const float4*)&stat[t & 1][1][g * 8 + hi * 4];
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
-            float pe[4], se[4];
+            for (int g = 0; g < 4; ++g) {
+                const float4 l4 = *(const float4*)&stat[t & 1][0][g * 8 + hi * 4];
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * g + e;
-                float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][r], sl2, -lv[e]));
-                if (masked) {
-                    const int qi = i0 + g * 8 + hi * 4 + e;
-                    bool vis = !CAUSAL || key <= qi;
-                    if constexpr (BAND)
-                        vis = vis && (p.wl < 0 || key >= qi - p.wl) && (p.wr < 0 || key <= qi + p.wr);
-                    pr = vis ? pr : 0.f;
-                }
-                pe[e] = pr;
-                se[e] = pr * (dp[0][r] - dvv[e]);
+                for (int e = 0; e < 4; ++e)
+                    s[0][4 * g + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][4 * g + e], sl2, -lv[e]));
             }
-            pkp[0][2 * g + 0] = pack_bf16x2(pe[0], pe[1]);
-            pkp[0][2 * g + 1] = pack_bf16x2(pe[2], pe[3]);
-            pks[0][2 * g + 0] = pack_bf16x2(se[0], se[1]);
-            pks[0][2 * g + 1] = pack_bf16x2(se[2], se[3]);
+            if (masked) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qi = i0 + (r >> 2) * 8 + hi * 4 + (r & 3);
+                    const bool vis = (!CAUSAL || key <= qi) && (p.wl < 0 || key >= qi - p.wl) &&
+                                     (p.wr < 0 || key <= qi + p.wr);
+                    s[0][r] = vis ? s[0][r] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 d4 = *(const float4*)&stat[t & 1][1][g * 8 + hi * 4];
+                const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+                float se[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) se[e] = s[0][4 * g + e] * (dp[0][4 * g + e] - dvv[e]);
+                pkp[0][2 * g + 0] = pack_bf16x2(s[0][4 * g + 0], s[0][4 * g + 1]);
+                pkp[0][2 * g + 1] = pack_bf16x2(s[0][4 * g + 2], s[0][4 * g + 3]);
+                pks[0][2 * g + 0] = pack_bf16x2(se[0], se[1]);
+                pks[0][2 * g + 1] = pack_bf16x2(se[2], se[3]);
+            }
+        } else {
+            // (written this way the compiler applies the causal mask's selects
+            // to every tile, but keeps every register; the branch form above
+            // spills here)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 l4 = *(const float4*)&stat[t & 1][0][g * 8 + hi * 4];
+                const float4 d4 = *(const float4*)&stat[t & 1][1][g * 8 + hi * 4];
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+                float pe[4], se[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e;
+                    float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][r], sl2, -lv[e]));
+                    if (masked) pr = key <= i0 + g * 8 + hi * 4 + e ? pr : 0.f;   // the causal diagonal
+                    pe[e] = pr;
+                    se[e] = pr * (dp[0][r] - dvv[e]);
+                }
+                pkp[0][2 * g + 0] = pack_bf16x2(pe[0], pe[1]);
+                pkp[0][2 * g + 1] = pack_bf16x2(pe[2], pe[3]);
+                pks[0][2 * g + 0] = pack_bf16x2(se[0], se[1]);
+                pks[0][2 * g + 1] = pack_bf16x2(se[2], se[3]);
+            }
         }
         tr_times_packed<D, 1>(dv, pkp, gst + (t & 1) * QTB, tr_row, tr_dd);
         tr_times_packed<D, 1>(dk, pks, qst + (t & 1) * QTB, tr_row, tr_dd);
