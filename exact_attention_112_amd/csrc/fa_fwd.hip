@@ -29,16 +29,20 @@
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (fp32 accumulate): a lane owns
 //     one query column, so the row max / row sum are in-lane plus one swap of
 //     the two 32-lane halves (v_permlane32_swap);
-//   * software pipeline inside each wave: while the matrix core computes the
-//     scores of key tile j+1, the vector ALU turns the scores of tile j into
-//     probabilities; while it computes O += P_j V_j, the vector ALU takes the
-//     row max of tile j+1.  Two waves per SIMD fill each other's gaps;
+//   * software pipeline inside each wave, its instruction order fixed by
+//     hand: while the matrix core computes the scores of key tile j+1, the
+//     vector ALU turns the scores of tile j into probabilities; while it
+//     computes O += P_j V_j, the vector ALU takes the row max of tile j+1;
+//     LDS fragments are read three MFMAs ahead.  Two waves per SIMD fill
+//     each other's gaps;
 //   * P stays in registers: rounded to bf16 (RNE, v_cvt_pk_bf16_f32) and fed as
 //     the B operand of O^T = V^T P^T; V^T fragments come straight from the
 //     row-major LDS tile through ds_read_b64_tr_b16 (transposing LDS read);
-//   * exp2 with scale*log2(e) folded into one FMA; the running max follows
-//     every increase, so the row's largest score so far always gets p = 1
-//     exactly and its bf16 rounding is exact;
+//   * exp2 with scale*log2(e) folded into one FMA; the running max moves
+//     only when a tile's max exceeds it by more than 2^8 in p, which makes
+//     rescaling the accumulator rare; the normaliser of O carries the bf16
+//     rounding error of each tile's largest p, so a row that one key
+//     dominates still gets exactly that key's V row;
 //   * epilogue: O = acc / l in fp32 (or bf16), LSE = (m2 + log2 l) * ln 2.
 // A plain fp32 kernel (v_mfma_f32_32x32x2f32, P kept in fp32) serves fp32
 // inputs; there the running max moves only when a tile's max exceeds it by
@@ -97,9 +101,21 @@ constexpr int kMaxSparseTiles = 4096;   // key tiles of 64 a block-sparse launch
 template <int D>
 struct RowState {
     f32x16 oacc[D / 32];
-    float m;          // running max of scale*log2(e)*s (same in both halves)
+    float m;          // running max of scale*log2(e)*s (same in both halves), kept
+                      // within kLazyMax below the true one
     float l0, l1;     // two partial sums of P over this lane's keys
+    float dl;         // sum of bf16(p) - p over the lane's largest score of each tile
+    float xl;         // this lane's largest raw score in the tile whose P is next
 };
+
+// The running max moves only when a tile's max exceeds it by more than this
+// (log2 units), so P lies in [0, 2^kLazyMax] and the accumulator is rescaled
+// only a few times per row.  The row's largest key then has p = 2^delta (not
+// exactly 1), whose bf16 rounding would leave a relative error of up to 2^-8
+// in O for a row that one key dominates; so the normaliser of O adds the
+// rounding error of each tile's largest p (dl), which makes that key's weight
+// exact again, while the LSE keeps the sum of the unrounded P.
+constexpr float kLazyMax = 8.0f;
 
 // S^T = K Q^T for one 64-key tile: 2 x D/16 MFMAs.
 template <int D>
@@ -148,7 +164,7 @@ __device__ __forceinline__ void mask_tile_band(f32x16 (&s)[2], int key0, int lo,
 
 // Row max of the tile, scaled to log2 units (the scale is > 0, so the max of
 // the scaled scores is the scaled max); -inf if every key of the row is masked.
-__device__ __forceinline__ float tile_max_scaled(const f32x16 (&s)[2], float sl2) {
+__device__ __forceinline__ float tile_max_scaled(const f32x16 (&s)[2], float sl2, float& lane_max) {
     // two chains of 3-input maxes (v_max3_f32), 8 each
     float a = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
     float b = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
@@ -157,7 +173,8 @@ __device__ __forceinline__ float tile_max_scaled(const f32x16 (&s)[2], float sl2
         a = fmaxf(fmaxf(a, s[0][r]), s[0][r + 1]);
         b = fmaxf(fmaxf(b, s[1][r]), s[1][r + 1]);
     }
-    return pair_max(fmaxf(fmaxf(a, s[0][15]), fmaxf(b, s[1][15]))) * sl2;
+    lane_max = fmaxf(fmaxf(a, s[0][15]), fmaxf(b, s[1][15]));
+    return pair_max(lane_max) * sl2;
 }
 
 // P = exp2(s*scale*log2e - m), accumulated into the two row-sum chains and
@@ -178,12 +195,21 @@ __device__ __forceinline__ void tile_exp(const f32x16 (&s)[2], float m, float sl
         }
 }
 
+// The rounding error bf16(p) - p of the lane's largest p in the tile (the p
+// that tile_exp computes for the score xl, with the same operations), added
+// to the normaliser of O.  -inf (all keys of the lane masked) gives 0.
+__device__ __forceinline__ void round_fix(float xl, float m, float sl2, float& dl) {
+    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(xl, sl2, -m));
+    const float r = __builtin_bit_cast(float, pack_bf16x2(0.0f, e) & 0xffff0000u);
+    dl += r - e;
+}
+
 // O^T += V^T P^T for one 64-key tile: 4 x D/32 MFMAs.  The lane's P slots
 // 0..3 of 16-key group u hold keys 16u + hi*4 + 0..3 and slots 4..7 keys
 // 16u + 8 + hi*4 + 0..3; the V^T fragment is read for the same keys.
 template <int D>
 __device__ __forceinline__ void pv_tile(f32x16 (&oacc)[D / 32], const unsigned (&pk)[2][8],
-                                        const lds_char* vs, int tr_row, int tr_dd) {
+                                        const lds_char* __restrict__ vs, int tr_row, int tr_dd) {
     constexpr int DB = D / 32;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -208,20 +234,22 @@ __device__ __forceinline__ void pv_tile(f32x16 (&oacc)[D / 32], const unsigned (
     }
 }
 
-// Move the running max to include a new tile whose scaled row max is mt2.
-// The rescale by alpha = exp2(m_old - m_new) is skipped by the whole wave when
-// no row's max moved (alpha would be 1 for every lane).
+// Take a new tile whose scaled row max is mt2 into the running max.  The
+// whole wave moves (every row to its true max, rescaling by alpha =
+// exp2(m_old - m_new)) when some row's tile max exceeds its running max by
+// more than kLazyMax; otherwise nothing changes.
 // SAFE: a row may have seen no visible key yet (m = -inf), so alpha is taken
 // as 1 where the max did not move instead of exp2(-inf - -inf).
 template <int D, bool SAFE = false>
 __device__ __forceinline__ void update_max(RowState<D>& st, float mt2) {
-    const bool move = mt2 > st.m;
-    if (__builtin_amdgcn_ballot_w64(move)) {
-        const float m_new = move ? mt2 : st.m;
+    if (__builtin_amdgcn_ballot_w64(mt2 > st.m + kLazyMax)) {
+        // every row of the wave moves to its true max
+        const float m_new = fmaxf(mt2, st.m);
         float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-        if constexpr (SAFE) alpha = move ? alpha : 1.0f;
+        if constexpr (SAFE) alpha = mt2 > st.m ? alpha : 1.0f;
         st.l0 *= alpha;
         st.l1 *= alpha;
+        st.dl *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -230,53 +258,89 @@ __device__ __forceinline__ void update_max(RowState<D>& st, float mt2) {
     }
 }
 
-// Instruction order of one pipelined step (one scheduling region), written
-// for the compiler's scheduler: phase A interleaves the scores of tile j+1
-// (one K fragment read and one MFMA at a time) with the exponentials of tile
-// j; phase B interleaves O += P V (two V^T fragment reads per MFMA) with the
-// row max of tile j+1.  LDS reads run two MFMAs ahead of their use.
-enum : unsigned { kSgVALU = 0x2, kSgMFMA = 0x8, kSgDSRead = 0x100, kSgTrans = 0x400 };
+// The same step with its instruction order fixed by hand (every group ends
+// in a scheduling fence): phase A issues each K fragment read three MFMAs
+// ahead of its use and runs two exponentials per score MFMA; its last three
+// groups already fetch the first V^T fragments; phase B issues each V^T
+// fragment three MFMAs ahead and takes the row max of tile j+1 in small
+// chunks once its scores have left the matrix core.
 template <int D>
-__device__ __forceinline__ void schedule_step() {
-    constexpr int NA = 2 * (D / 16);   // QK MFMAs
-    constexpr int NB = 4 * (D / 32);   // PV MFMAs
-    constexpr int VA = 80 / NA, TA = 32 / NA;
-    __builtin_amdgcn_sched_group_barrier(kSgDSRead, 2, 0);
+__device__ __forceinline__ void wave_step_sw(RowState<D>& st, const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+                                             const bf16x8 (&qreg)[D / 16], const u32x4* __restrict__ ks,
+                                             const lds_char* __restrict__ vs, float sl2, int col, int hi,
+                                             int tr_row, int tr_dd) {
+    constexpr int DCH = D / 8, DB = D / 32;
+    constexpr int NA = 2 * (D / 16);      // score MFMAs
+    constexpr int NB = 4 * DB;            // P V MFMAs
+    constexpr int PPM = 16 / NA;          // exponential pairs per score MFMA
+    constexpr int CPS = NB == 16 ? 1 : 2; // max chunks per P V MFMA
+    auto kread = [&](int i) -> bf16x8 {
+        const int kk = i >> 1, kb = i & 1, row = kb * 32 + col;
+        return __builtin_bit_cast(bf16x8, ks[row * DCH + k_swz<D>(row, 2 * kk + hi)]);
+    };
+    auto vread = [&](int i) -> bf16x8 {
+        const int kb = i / (2 * DB), u = (i / DB) & 1, db = i % DB;
+        const int r0 = kb * 32 + 16 * u + tr_row, r1 = r0 + 8;
+        const int dd = db * 32 + tr_dd, c = dd >> 3, w = (dd & 7) * 2;
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vs + r0 * (D * 2) + v_swz<D>(r0, c) * 16 + w));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vs + r1 * (D * 2) + v_swz<D>(r1, c) * 16 + w));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    const float nm = -st.m;
+    unsigned pk[2][8];
+    bf16x8 kf[4], vf[4];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) kf[i] = kread(i);
+    __builtin_amdgcn_sched_barrier(0);
+    // phase A
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSgMFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgVALU, VA, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgTrans, TA, 0);
-        if (i + 2 < NA) __builtin_amdgcn_sched_group_barrier(kSgDSRead, 1, 0);
+        if (i + 3 < NA) kf[(i + 3) & 3] = kread(i + 3);
+        else vf[i + 3 - NA] = vread(i + 3 - NA);
+        const int kb = i & 1;
+        s_nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], qreg[i >> 1], i < 2 ? f32x16{} : s_nxt[kb],
+                                                            0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < PPM; ++e) {
+            const int pr = i * PPM + e, b = pr >> 3, jj = pr & 7;
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][2 * jj], sl2, nm));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][2 * jj + 1], sl2, nm));
+            st.l0 += e0;
+            st.l1 += e1;
+            pk[b][jj] = pack_bf16x2(e0, e1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(kSgDSRead, 4, 0);
+    // phase B
+    float a = 0.f, bm = 0.f, mt2 = 0.f, xl_new = 0.f;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSgMFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgVALU, 2, 0);
-        if (i + 2 < NB) __builtin_amdgcn_sched_group_barrier(kSgDSRead, 2, 0);
+        if (i + 3 < NB) vf[(i + 3) & 3] = vread(i + 3);
+        const int kb = i / (2 * DB), u = (i / DB) & 1, db = i % DB;
+        const bf16x8 pb = __builtin_bit_cast(
+            bf16x8, (u32x4){pk[kb][4 * u + 0], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]});
+        st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 3], pb, st.oacc[db], 0, 0, 0);
+#pragma unroll
+        for (int cc = 0; cc < CPS; ++cc) {
+            const int c = (i - 2) * CPS + cc;   // max chunk 0..7
+            if (i >= 2 && c == 0) {
+                a = fmaxf(fmaxf(s_nxt[0][0], s_nxt[0][1]), s_nxt[0][2]);
+                bm = fmaxf(fmaxf(s_nxt[1][0], s_nxt[1][1]), s_nxt[1][2]);
+            } else if (i >= 2 && c >= 1 && c <= 6) {
+                a = fmaxf(fmaxf(a, s_nxt[0][2 * c + 1]), s_nxt[0][2 * c + 2]);
+                bm = fmaxf(fmaxf(bm, s_nxt[1][2 * c + 1]), s_nxt[1][2 * c + 2]);
+            } else if (i >= 2 && c == 7) {
+                xl_new = fmaxf(fmaxf(a, s_nxt[0][15]), fmaxf(bm, s_nxt[1][15]));
+            }
+        }
+        if (i == 2 + 8 / CPS) mt2 = pair_max(xl_new) * sl2;
+        if (i == 3 + 8 / CPS) round_fix(st.xl, st.m, sl2, st.dl);
+        __builtin_amdgcn_sched_barrier(0);
     }
-}
-
-// One pipelined step of a wave: probabilities of tile j (scores in s_cur,
-// the running max already includes tile j) and O += P_j V_j, overlapped with
-// the scores of tile j+1 (into s_nxt) and their row max.
-//   ks_nxt: K tile j+1 in LDS; vs_cur: V tile j in LDS (bytes)
-template <int D, bool CAUSAL, bool MASK_NXT, bool HAS_NXT>
-__device__ __forceinline__ void wave_step(RowState<D>& st, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
-                                          const bf16x8 (&qreg)[D / 16], const u32x4* ks_nxt,
-                                          const lds_char* vs_cur, int key0_nxt, int q, int Nk, float sl2,
-                                          int col, int hi, int tr_row, int tr_dd) {
-    unsigned pk[2][8];
-    if constexpr (HAS_NXT) qk_tile<D>(s_nxt, qreg, ks_nxt, col, hi);
-    tile_exp(s_cur, st.m, sl2, pk, st.l0, st.l1);
-    pv_tile<D>(st.oacc, pk, vs_cur, tr_row, tr_dd);
-    if constexpr (HAS_NXT) {
-        if constexpr (MASK_NXT) mask_tile<CAUSAL>(s_nxt, key0_nxt, q, Nk, hi);
-        const float mt2 = tile_max_scaled(s_nxt, sl2);
-        schedule_step<D>();
-        update_max(st, mt2);
-    }
+    st.xl = xl_new;
+    update_max(st, mt2);
 }
 
 // The same step without the overlap, for the few masked tiles at the end:
@@ -289,11 +353,12 @@ __device__ __forceinline__ void wave_step_serial(RowState<D>& st, f32x16 (&s)[2]
                                                  int Nk, float sl2, int col, int hi, int tr_row, int tr_dd) {
     unsigned pk[2][8];
     tile_exp(s, st.m, sl2, pk, st.l0, st.l1);
+    round_fix(st.xl, st.m, sl2, st.dl);
     pv_tile<D>(st.oacc, pk, vs_cur, tr_row, tr_dd);
     if constexpr (HAS_NXT) {
         qk_tile<D>(s, qreg, ks_nxt, col, hi);
         mask_tile<CAUSAL>(s, key0_nxt, q, Nk, hi);
-        update_max(st, tile_max_scaled(s, sl2));
+        update_max(st, tile_max_scaled(s, sl2, st.xl));
     }
 }
 
@@ -305,12 +370,14 @@ __device__ __forceinline__ void wave_step_band(RowState<D>& st, f32x16 (&s)[2], 
                                                const u32x4* ks_nxt, const lds_char* vs_cur, int key0_nxt, int lo,
                                                int hi_key, float sl2, int col, int hi, int tr_row, int tr_dd) {
     unsigned pk[2][8];
-    tile_exp(s, fmaxf(st.m, -3.0e38f), sl2, pk, st.l0, st.l1);
+    const float m_fin = fmaxf(st.m, -3.0e38f);
+    tile_exp(s, m_fin, sl2, pk, st.l0, st.l1);
+    round_fix(st.xl, m_fin, sl2, st.dl);
     pv_tile<D>(st.oacc, pk, vs_cur, tr_row, tr_dd);
     if constexpr (HAS_NXT) {
         qk_tile<D>(s, qreg, ks_nxt, col, hi);
         mask_tile_band(s, key0_nxt, lo, hi_key, hi);
-        update_max<D, true>(st, tile_max_scaled(s, sl2));
+        update_max<D, true>(st, tile_max_scaled(s, sl2, st.xl));
     }
 }
 
@@ -494,6 +561,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     st.m = -INFINITY;
     st.l0 = 0.f;
     st.l1 = 0.f;
+    st.dl = 0.f;
+    st.xl = -INFINITY;
     const float sl2 = p.scale_log2;
 
     // V^T fragment addressing for ds_read_b64_tr_b16: within each 16-lane
@@ -525,7 +594,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         } else {
             if (n_full == 0) mask_tile<CAUSAL>(sa, 0, q, Nk, hi);
         }
-        st.m = tile_max_scaled(sa, sl2);
+        st.m = tile_max_scaled(sa, sl2, st.xl);
     }
 
 #define FA_TOP(j)                                      \
@@ -558,11 +627,9 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // score buffers swap roles without copies.
     for (; j + 2 < n_full; j += 2) {
         FA_TOP(j);
-        wave_step<D, CAUSAL, false, true>(st, sa, sb, qreg, FA_KS(j + 1), FA_V_STAGE(j), 0, q, Nk, sl2, col, hi,
-                                          tr_row, tr_dd);
+        wave_step_sw<D>(st, sa, sb, qreg, FA_KS(j + 1), FA_V_STAGE(j), sl2, col, hi, tr_row, tr_dd);
         FA_TOP(j + 1);
-        wave_step<D, CAUSAL, false, true>(st, sb, sa, qreg, FA_KS(j + 2), FA_V_STAGE(j + 1), 0, q, Nk, sl2, col,
-                                          hi, tr_row, tr_dd);
+        wave_step_sw<D>(st, sb, sa, qreg, FA_KS(j + 2), FA_V_STAGE(j + 1), sl2, col, hi, tr_row, tr_dd);
     }
     // The remaining steps (at most a few): masks on, per-wave skips, no
     // overlap (one score buffer).
@@ -597,11 +664,12 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 
     // ---- epilogue
     const float l_tot = pair_sum(st.l0 + st.l1);
+    const float dl_tot = pair_sum(st.dl);
     // the lane's half, recomputed (mbcnt) rather than kept live through the loops
     const int hi_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5;
     if (q < Nq) {
         // (band: a row that saw no key has l = 0 and gets O = 0, LSE = -inf)
-        const float inv = (!SAFE || l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+        const float inv = (!SAFE || l_tot > 0.f) ? 1.0f / (l_tot + dl_tot) : 0.f;
         char* obase = (char*)p.o;
         const long long orow = (long long)b * p.q_sb + (long long)h * p.q_sh + (long long)q * p.q_sn;
 #pragma unroll
