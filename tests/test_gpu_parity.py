@@ -205,6 +205,38 @@ def test_closed_forms():
     assert (o - v[:, :, 37:38].float()).abs().max().item() < 1e-3
 
 
+def test_dominant_key_below_the_rescale_threshold():
+    """A later key outscores the first tile's max by about 5.3 in log2 units:
+    the running max stays where the first tile put it, so that key's p is
+    about 39 and its bf16 rounding is not exact.  The row is dominated by it
+    (weight ~0.97) and its V row is large, so O is right to 1e-2 only if the
+    normaliser accounts for that rounding."""
+    import torch
+    import exact_attention_112_amd as fa
+    require_gpu()
+    B, H, N, d = 1, 2, 256, 128
+    scale = 1.0 / math.sqrt(d)
+    rng = np.random.default_rng(11)
+    q = np.zeros((B, H, N, d))
+    q[..., 0] = 4.0
+    k = np.zeros((B, H, N, d))
+    k[..., 0] = -30.0            # negligible keys
+    k[..., 0, 0] = 1.0           # first tile's max
+    hot = (100, 230)             # the near-dominant key, in tile 1 / tile 3
+    v = rng.standard_normal((B, H, N, d))
+    v[..., 0, :] = 0.0
+    for h, j in enumerate(hot):
+        k[0, h, j, 0] = 11.375   # exact in bf16; 4 * 10.375 * scale * log2(e) = 5.29 above key 0
+        v[0, h, j, :] = 16.0 * np.where(np.arange(d) % 2 == 0, 1.0, -1.0)
+    to_bf16 = lambda a: torch.from_numpy(a).float().bfloat16().cuda()
+    tq, tk, tv = to_bf16(q), to_bf16(k), to_bf16(v)
+    o, lse = fa.fwd(tq, tk, tv, causal=False, scale=scale)
+    wide = lambda t: t.float().cpu().numpy().astype(np.float64)
+    o_ref, lse_ref = oracle.attn_fwd(wide(tq), wide(tk), wide(tv), scale=scale, causal=False, layout="BHND")
+    err = errors(wide(o), wide(lse), o_ref, lse_ref)
+    check(err, BF16_TOL, "dominant key below the rescale threshold")
+
+
 # ---------------------------------------------------------------------------
 # API behaviour
 
