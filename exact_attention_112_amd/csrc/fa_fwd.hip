@@ -39,7 +39,7 @@
 //     the B operand of O^T = V^T P^T; V^T fragments come straight from the
 //     row-major LDS tile through ds_read_b64_tr_b16 (transposing LDS read);
 //   * exp2 with scale*log2(e) folded into one FMA; the running max moves
-//     only when a tile's max exceeds it by more than 2^8 in p, which makes
+//     only when a tile's max exceeds it by more than 2^4 in p, which makes
 //     rescaling the accumulator rare; the normaliser of O carries the bf16
 //     rounding error of each tile's largest p, so a row that one key
 //     dominates still gets exactly that key's V row;
@@ -115,7 +115,7 @@ struct RowState {
 // in O for a row that one key dominates; so the normaliser of O adds the
 // rounding error of each tile's largest p (dl), which makes that key's weight
 // exact again, while the LSE keeps the sum of the unrounded P.
-constexpr float kLazyMax = 8.0f;
+constexpr float kLazyMax = 4.0f;
 
 // S^T = K Q^T for one 64-key tile: 2 x D/16 MFMAs.
 template <int D>
