@@ -272,8 +272,14 @@ __device__ __forceinline__ void wave_step_sw(RowState<D>& st, const f32x16 (&s_c
     constexpr int DCH = D / 8, DB = D / 32;
     constexpr int NA = 2 * (D / 16);      // score MFMAs
     constexpr int NB = 4 * DB;            // P V MFMAs
-    constexpr int PPM = 16 / NA;          // exponential pairs per score MFMA
+    // exponential pairs (16 per tile): PA of them in phase A, PPM per score
+    // MFMA; the rest in the first groups of phase B, before the P V MFMAs
+    // that need them (d = 128: 12 + 4, which spreads the vector work more
+    // evenly over the two phases)
+    constexpr int PA = D == 128 ? 12 : 16;
+    constexpr int PPM = PA / NA > 0 ? PA / NA : 1;
     constexpr int CPS = NB == 16 ? 1 : 2; // max chunks per P V MFMA
+    constexpr int MS = 16 - PA > 2 ? 16 - PA : 2;   // first group of the max chunks
     auto kread = [&](int i) -> bf16x8 {
         const int kk = i >> 1, kb = i & 1, row = kb * 32 + col;
         return __builtin_bit_cast(bf16x8, ks[row * DCH + k_swz<D>(row, 2 * kk + hi)]);
@@ -305,11 +311,13 @@ __device__ __forceinline__ void wave_step_sw(RowState<D>& st, const f32x16 (&s_c
 #pragma unroll
         for (int e = 0; e < PPM; ++e) {
             const int pr = i * PPM + e, b = pr >> 3, jj = pr & 7;
-            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][2 * jj], sl2, nm));
-            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][2 * jj + 1], sl2, nm));
-            st.l0 += e0;
-            st.l1 += e1;
-            pk[b][jj] = pack_bf16x2(e0, e1);
+            if (pr < PA) {
+                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][2 * jj], sl2, nm));
+                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][2 * jj + 1], sl2, nm));
+                st.l0 += e0;
+                st.l1 += e1;
+                pk[b][jj] = pack_bf16x2(e0, e1);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -322,21 +330,29 @@ __device__ __forceinline__ void wave_step_sw(RowState<D>& st, const f32x16 (&s_c
         const bf16x8 pb = __builtin_bit_cast(
             bf16x8, (u32x4){pk[kb][4 * u + 0], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]});
         st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 3], pb, st.oacc[db], 0, 0, 0);
+        if (PA + i < 16) {
+            const int pr = PA + i, b = pr >> 3, jj = pr & 7;
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][2 * jj], sl2, nm));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][2 * jj + 1], sl2, nm));
+            st.l0 += e0;
+            st.l1 += e1;
+            pk[b][jj] = pack_bf16x2(e0, e1);
+        }
 #pragma unroll
         for (int cc = 0; cc < CPS; ++cc) {
-            const int c = (i - 2) * CPS + cc;   // max chunk 0..7
-            if (i >= 2 && c == 0) {
+            const int c = (i - MS) * CPS + cc;   // max chunk 0..7
+            if (i >= MS && c == 0) {
                 a = fmaxf(fmaxf(s_nxt[0][0], s_nxt[0][1]), s_nxt[0][2]);
                 bm = fmaxf(fmaxf(s_nxt[1][0], s_nxt[1][1]), s_nxt[1][2]);
-            } else if (i >= 2 && c >= 1 && c <= 6) {
+            } else if (i >= MS && c >= 1 && c <= 6) {
                 a = fmaxf(fmaxf(a, s_nxt[0][2 * c + 1]), s_nxt[0][2 * c + 2]);
                 bm = fmaxf(fmaxf(bm, s_nxt[1][2 * c + 1]), s_nxt[1][2 * c + 2]);
-            } else if (i >= 2 && c == 7) {
+            } else if (i >= MS && c == 7) {
                 xl_new = fmaxf(fmaxf(a, s_nxt[0][15]), fmaxf(bm, s_nxt[1][15]));
             }
         }
-        if (i == 2 + 8 / CPS) mt2 = pair_max(xl_new) * sl2;
-        if (i == 3 + 8 / CPS) round_fix(st.xl, st.m, sl2, st.dl);
+        if (i == MS + 8 / CPS) mt2 = pair_max(xl_new) * sl2;
+        if (i == MS + 1 + 8 / CPS) round_fix(st.xl, st.m, sl2, st.dl);
         __builtin_amdgcn_sched_barrier(0);
     }
     st.xl = xl_new;
