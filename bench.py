@@ -12,9 +12,21 @@ throughput in TFLOP/s (4*B*H*Nq*Nk*d, halved for causal) and:
   (2.5 PFLOP/s), timed live with HIP events on the stream the kernel runs on;
   ``traffic`` is the HBM bytes per launch from the committed rocprofv3 counter
   summary, or null when the kernel source changed since it was taken;
+* latency_ms: mean, median, min and max of the per-launch times (HIP events
+  around each launch), and the TFLOP/s at the median;
+* counters: the matrix-core busy fraction, vector-ALU busy fraction, LDS bank
+  conflicts and HBM rate from the committed rocprofv3 counter summary of the
+  current kernel source (null otherwise);
 * cpu_baseline: the fp64 CPU oracle timed on this host's cores on a bounded
   sample of the same workload (rows of the first heads, about 10 s of work),
-  as a reported baseline, not a target.
+  with the host's CPU model and core counts and the extrapolated time of a
+  full oracle run, as a reported baseline, not a target;
+* context: the pages' own latency figures with their hardware (Ascend 910B,
+  Atlas 800), for context only.
+
+``--workload all`` runs the five forward workloads one after another (30
+timed launches after 5 warmup launches; 10 after 2 for the 128K context),
+prints one line each and, with ``--out PATH``, writes them to a JSON file.
 
 With ``--pass bwd`` one step is one fa_bwd call (D = rowsum(dO*O), the dK/dV
 kernel and the dQ kernel) on the workload, given O and LSE from one forward
@@ -40,6 +52,9 @@ BWD_METRIC = "attention bwd TFLOPS and % of bf16 MFMA peak at B4 H32 N8192 d128"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA (published)
 PEAK_F32_TFLOPS = 157.3            # MI355X fp32 (matrix and vector), published
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
+# the five forward workloads (tiny fp32, causal prefill, the headline
+# self-attention, cross-attention on 77 keys, the 128K causal context)
+FORWARD_WORKLOADS = ["tiny_f32", "llama_prefill_causal", "selfattn_b4h32n8k", "sd_crossattn", "long_causal_128k"]
 
 
 def bwd_algorithmic_bytes(w) -> float:
@@ -88,15 +103,75 @@ def traffic_from_profiles(workload: str, which: str = "fwd"):
     return float(m_bytes.group(1))
 
 
+def counters_from_profiles(workload: str, which: str = "fwd"):
+    """The SQ counter figures (matrix-core busy, vector-ALU busy, LDS bank
+    conflicts, HBM rate) recorded in profiles/fa_<which>_<workload>_counters.md
+    for the current kernel source, or None."""
+    path = os.path.join(PROFILES, f"fa_{which}_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m_hash or m_hash.group(1) != kernel_source_hash(which):
+        return None
+    out = {}
+    for key in ("mfma_busy_frac", "valu_busy_frac", "lds_bank_conflict_frac", "hbm_gbs", "clock_ghz"):
+        m = re.search(rf"{key}:\s*([0-9.eE+-]+)", text)
+        if m:
+            out[key] = float(m.group(1))
+    return out or None
+
+
+def host_cpu():
+    """The host's CPU model and core counts (for the CPU baseline's record)."""
+    model, cores = None, set()
+    try:
+        phys = core = None
+        for line in open("/proc/cpuinfo"):
+            key, _, val = line.partition(":")
+            key, val = key.strip(), val.strip()
+            if key == "model name" and model is None:
+                model = val
+            elif key == "physical id":
+                phys = val
+            elif key == "core id":
+                core = val
+                cores.add((phys, core))
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "physical_cores": len(cores) or None, "logical_cpus": os.cpu_count(),
+            "usable_cpus": usable, "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+# The pages' own latency figures for this path, with their hardware: other
+# machines, precision and masking not stated, so context only (not a target).
+PAGES_CONTEXT = [
+    {"source": "[pwwt] www.pwwt.cn/news/2518640, section on measured performance",
+     "hardware": "Huawei Ascend 910B", "workload": "LLaMA-13B inference (batch and masking not stated)",
+     "seq_len": [2048, 4096, 8192], "flash_attention_ms": [18, 38, 82], "standard_attention_ms": [42, 156, "OOM"]},
+    {"source": "[ascendai] ascendai.csdn.net, section 4.3 (performance comparison)",
+     "hardware": "Huawei Atlas 800", "workload": "B=4 H=32 D=128 (masking not stated)",
+     "seq_len": [2048, 8192, 32768, 131072], "flash_attention_ms": [6.2, 24, 95, 380],
+     "standard_attention_ms": [8.5, 125, "OOM", "OOM"]},
+]
+
+
 def cpu_baseline(w, inp, target_s: float = 10.0):
-    """Time the fp64 oracle on rows 0, 4, 8, ... of consecutive heads until at
-    least ``target_s`` seconds of work are done (bounded by the workload)."""
+    """Time the fp64 oracle on every 4th query row (every Nq/2048-th on longer
+    sequences) of consecutive heads until at least ``target_s`` seconds of
+    work are done (bounded by the workload); also extrapolates the time of a
+    full oracle run by the flop ratio (an estimate)."""
     import numpy as np
     import oracle
 
     lib = oracle.lib()
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or lib.max_threads()
-    rows = np.arange(0, w.Nq, 4, dtype=np.int32)
+    stride = max(4, w.Nq // 2048)                # at most 2048 rows of a head
+    rows = np.arange(0, w.Nq, stride, dtype=np.int32)
     heads_per_chunk = 2
     done_heads, flops, elapsed = 0, 0.0, 0.0
     total_heads = w.B * w.H
@@ -137,9 +212,11 @@ def cpu_baseline(w, inp, target_s: float = 10.0):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"fp64 two-pass oracle on every 4th query row ({len(rows)} rows) of the first "
+        "sample": (f"fp64 two-pass oracle on every {stride}th query row ({len(rows)} rows) of the first "
                    f"{done_heads} of {total_heads} heads of {w.name}; {flops:.3e} flop in "
                    f"{elapsed:.1f} s on {threads} threads"),
+        "host": host_cpu(),
+        "full_run_s_estimate": round(w.flops / (flops / elapsed), 1),
     }
 
 
@@ -372,17 +449,156 @@ def bench_decode(args, w):
     return 0
 
 
+def bench_attention(args, w, steps: int, warmup: int, with_cpu: bool):
+    """Time ``steps`` calls of the forward (or, with args.which == "bwd", the
+    backward) pass on workload ``w`` after ``warmup`` untimed calls; returns
+    the JSON record (None on a non-finite output).  Each launch is bracketed
+    by HIP events on the stream the kernels run on; ``ms_per_step`` is the
+    mean over the timed launches (back to back, no cache flush)."""
+    import numpy as np
+    import torch
+    import exact_attention_112_amd as fa
+    from exact_attention_112_amd import inputs as I
+
+    print(f"bench: generating inputs for {w.name}", file=sys.stderr, flush=True)
+    inp = I.make_inputs(w)
+    if w.dtype == "bf16":
+        up = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda")
+        tq, tk, tv = up(inp.q_bits), up(inp.k_bits), up(inp.v_bits)
+    else:
+        tq, tk, tv = (torch.from_numpy(x).to("cuda") for x in (inp.q, inp.k, inp.v))
+    out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
+    o = torch.empty(tq.shape, dtype=out_dtype, device="cuda")
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+
+    bmask, sparse_flops = None, None
+    if w.block_sparse:
+        mask_np = I.make_block_mask(w)
+        bmask = torch.from_numpy(mask_np).to("cuda")
+        sparse_flops = sparse_pair_flops(w, mask_np)
+
+    def step():
+        fa.fwd(tq, tk, tv, causal=w.causal, scale=w.scale, layout=w.layout, out_dtype=out_dtype,
+               out=o, lse=lse, window=None if w.window == (-1, -1) else w.window, block_mask=bmask)
+
+    if args.which == "bwd":
+        if w.dtype != "bf16":
+            print("bench.py: the backward pass takes bf16 inputs", file=sys.stderr)
+            return None
+        grad_vals, grad_bits = I.make_grad(w)
+        tdo = up(grad_bits)
+        step()                                   # O and LSE for the backward, untimed
+        dq = torch.empty(tq.shape, dtype=torch.float32, device="cuda")
+        dk = torch.empty(tk.shape, dtype=torch.float32, device="cuda")
+        dv = torch.empty(tk.shape, dtype=torch.float32, device="cuda")
+        delta = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+
+        def step():  # noqa: F811  (the timed step of the backward benchmark)
+            fa.bwd(tq, tk, tv, o, tdo, lse, causal=w.causal, scale=w.scale, layout=w.layout,
+                   window=None if w.window == (-1, -1) else w.window, block_mask=bmask, dq=dq, dk=dk, dv=dv,
+                   delta=delta)
+
+    print(f"bench: warmup {warmup}", file=sys.stderr, flush=True)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()        # the stream fa.fwd / fa.bwd launch on
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    print(f"bench: timing {steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    ms = ev[0].elapsed_time(ev[steps]) / steps
+    srt = sorted(per)
+    latency = {"mean": round(ms, 4), "median": round(srt[len(srt) // 2] if len(srt) % 2 else
+                                                     0.5 * (srt[len(srt) // 2 - 1] + srt[len(srt) // 2]), 4),
+               "min": round(srt[0], 4), "max": round(srt[-1], 4)}
+    bwd = args.which == "bwd"
+    fwd_flops = sparse_flops if w.block_sparse else w.flops
+    flops = 2.5 * fwd_flops if bwd else fwd_flops
+    tflops = flops / (ms * 1e-3) / 1e12
+    outs = (dq, dk, dv) if bwd else (o, lse)
+    if not all(torch.isfinite(t).all() for t in outs):
+        print("bench: non-finite output", file=sys.stderr)
+        return None
+
+    cpu = None
+    if with_cpu:
+        print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        if bwd and w.block_sparse:
+            cpu = cpu_baseline_bwd_sparse(w, inp, grad_vals, mask_np)
+        elif bwd:
+            cpu = cpu_baseline_bwd(w, inp, grad_vals)
+        elif w.block_sparse:
+            cpu = cpu_baseline_sparse(w, inp, mask_np)
+        else:
+            cpu = cpu_baseline(w, inp)
+
+    traffic = traffic_from_profiles(w.name, args.which)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    nbytes = bwd_algorithmic_bytes(w) if bwd else algorithmic_bytes(w, 2 if args.out_dtype == "bf16" else 4)
+    if flops / nbytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        gbs = nbytes / (ms * 1e-3) / 1e9     # below the ridge point: HBM-bound
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tflops / peak, 4), "traffic": traffic}
+    line = {
+        "metric": ((BWD_METRIC if bwd else METRIC) if w.name == "selfattn_b4h32n8k"
+                   else f"attention {args.which} TFLOPS and % of bf16 MFMA peak at {w.name}"),
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": ("synthetic (seeded N(0,1) Q/K/V/dO of the workload's shape, seeded BigBird-like block mask; "
+                 "O, LSE from the GPU forward)" if w.block_sparse and bwd else
+                 "synthetic (seeded N(0,1) Q/K/V of the workload's shape, seeded BigBird-like block mask)"
+                 if w.block_sparse else
+                 "synthetic (seeded N(0,1) Q/K/V/dO of the workload's shape; O, LSE from the GPU forward)"
+                 if bwd else "synthetic (seeded N(0,1) Q/K/V of the workload's shape)"),
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "layout": w.layout, "out_dtype": args.out_dtype,
+                   **({"Hkv": w.kv_heads, "window": list(w.window)}
+                      if w.kv_heads != w.H or w.window != (-1, -1) else {}),
+                   **({"block_sparse": True, "mask_density": round(float(mask_np.mean()), 4)}
+                      if w.block_sparse else {}),
+                   **({"pass": "bwd", "grads": "f32"} if bwd else {})},
+        "latency_ms": latency,
+        "tflops_at_median": round(flops / (latency["median"] * 1e-3) / 1e12, 2),
+        "roofline": roof,
+        "counters": counters_from_profiles(w.name, args.which),
+        "cpu_baseline": cpu,
+        "context": {"peak_note": "MI355X published dense peaks: bf16 MFMA 2.5 PFLOP/s, HBM 8 TB/s",
+                    "pages": PAGES_CONTEXT},
+    }
+    return line
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="selfattn_b4h32n8k")
+    ap.add_argument("--workload", default="selfattn_b4h32n8k",
+                    help="a workload name, or 'all' for the five forward workloads one after another")
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
                     help="time the forward pass (default) or the backward pass")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
+    ap.add_argument("--out", default=None, metavar="PATH",
+                    help="with --workload all: also write every record to this JSON file")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 3 times (the "
                          "reference for scaling HBM counters), then exit")
@@ -413,120 +629,29 @@ def main(argv=None):
     fa.load()
     if args.workload in I.DECODE_WORKLOADS:
         return bench_decode(args, I.DECODE_WORKLOADS[args.workload])
-    w = I.WORKLOADS[args.workload]
-    print(f"bench: generating inputs for {w.name}", file=sys.stderr, flush=True)
-    inp = I.make_inputs(w)
-    if w.dtype == "bf16":
-        up = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda")
-        tq, tk, tv = up(inp.q_bits), up(inp.k_bits), up(inp.v_bits)
-    else:
-        tq, tk, tv = (torch.from_numpy(x).to("cuda") for x in (inp.q, inp.k, inp.v))
-    out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
-    o = torch.empty(tq.shape, dtype=out_dtype, device="cuda")
-    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
-
-    bmask, sparse_flops = None, None
-    if w.block_sparse:
-        mask_np = I.make_block_mask(w)
-        bmask = torch.from_numpy(mask_np).to("cuda")
-        sparse_flops = sparse_pair_flops(w, mask_np)
-
-    def step():
-        fa.fwd(tq, tk, tv, causal=w.causal, scale=w.scale, layout=w.layout, out_dtype=out_dtype,
-               out=o, lse=lse, window=None if w.window == (-1, -1) else w.window, block_mask=bmask)
-
-    if args.which == "bwd":
-        if w.dtype != "bf16":
-            print("bench.py: the backward pass takes bf16 inputs", file=sys.stderr)
-            return 2
-        grad_vals, grad_bits = I.make_grad(w)
-        tdo = up(grad_bits)
-        step()                                   # O and LSE for the backward, untimed
-        dq = torch.empty(tq.shape, dtype=torch.float32, device="cuda")
-        dk = torch.empty(tk.shape, dtype=torch.float32, device="cuda")
-        dv = torch.empty(tk.shape, dtype=torch.float32, device="cuda")
-        delta = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
-
-        def step():  # noqa: F811  (the timed step of the backward benchmark)
-            fa.bwd(tq, tk, tv, o, tdo, lse, causal=w.causal, scale=w.scale, layout=w.layout,
-                   window=None if w.window == (-1, -1) else w.window, block_mask=bmask, dq=dq, dk=dk, dv=dv,
-                   delta=delta)
-
-    print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    print(f"bench: timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    bwd = args.which == "bwd"
-    fwd_flops = sparse_flops if w.block_sparse else w.flops
-    flops = 2.5 * fwd_flops if bwd else fwd_flops
-    tflops = flops / (ms * 1e-3) / 1e12
-    outs = (dq, dk, dv) if bwd else (o, lse)
-    if not all(torch.isfinite(t).all() for t in outs):
-        print("bench: non-finite output", file=sys.stderr)
+    names = FORWARD_WORKLOADS if args.workload == "all" else [args.workload]
+    if args.workload == "all" and args.which != "fwd":
+        print("bench.py: --workload all times the forward pass", file=sys.stderr)
+        return 2
+    if args.workload == "all":
+        records = []
+        for name in names:
+            w = I.WORKLOADS[name]
+            steps, warmup = (10, 2) if w.Nq >= 65536 else (30, 5)
+            rec = bench_attention(args, w, steps, warmup, with_cpu=not args.no_cpu_baseline)
+            if rec is None:
+                return 1
+            print(json.dumps(rec), flush=True)
+            records.append(rec)
+        if args.out:
+            with open(args.out, "w") as f:
+                json.dump({"records": records}, f, indent=1)
+        return 0
+    rec = bench_attention(args, I.WORKLOADS[args.workload], args.steps, args.warmup,
+                          with_cpu=not args.no_cpu_baseline)
+    if rec is None:
         return 1
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        if bwd and w.block_sparse:
-            cpu = cpu_baseline_bwd_sparse(w, inp, grad_vals, mask_np)
-        elif bwd:
-            cpu = cpu_baseline_bwd(w, inp, grad_vals)
-        elif w.block_sparse:
-            cpu = cpu_baseline_sparse(w, inp, mask_np)
-        else:
-            cpu = cpu_baseline(w, inp)
-
-    traffic = traffic_from_profiles(w.name, args.which)
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    nbytes = bwd_algorithmic_bytes(w) if bwd else algorithmic_bytes(w, 2 if args.out_dtype == "bf16" else 4)
-    if flops / nbytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9):
-        gbs = nbytes / (ms * 1e-3) / 1e9     # below the ridge point: HBM-bound
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
-    else:
-        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(tflops / peak, 4), "traffic": traffic}
-    line = {
-        "metric": ((BWD_METRIC if bwd else METRIC) if w.name == "selfattn_b4h32n8k"
-                   else f"attention {args.which} TFLOPS and % of bf16 MFMA peak at {w.name}"),
-        "value": round(tflops, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": ("synthetic (seeded N(0,1) Q/K/V/dO of the workload's shape, seeded BigBird-like block mask; "
-                 "O, LSE from the GPU forward)" if w.block_sparse and bwd else
-                 "synthetic (seeded N(0,1) Q/K/V of the workload's shape, seeded BigBird-like block mask)"
-                 if w.block_sparse else
-                 "synthetic (seeded N(0,1) Q/K/V/dO of the workload's shape; O, LSE from the GPU forward)"
-                 if bwd else "synthetic (seeded N(0,1) Q/K/V of the workload's shape)"),
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
-                   "causal": w.causal, "layout": w.layout, "out_dtype": args.out_dtype,
-                   **({"Hkv": w.kv_heads, "window": list(w.window)}
-                      if w.kv_heads != w.H or w.window != (-1, -1) else {}),
-                   **({"block_sparse": True, "mask_density": round(float(mask_np.mean()), 4)}
-                      if w.block_sparse else {}),
-                   **({"pass": "bwd", "grads": "f32"} if bwd else {})},
-        "roofline": roof,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(line), flush=True)
+    print(json.dumps(rec), flush=True)
     return 0
 
 

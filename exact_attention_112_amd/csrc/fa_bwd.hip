@@ -219,6 +219,9 @@ template <int D, bool CAUSAL, bool BAND, bool GQA, bool SPARSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
     constexpr int NW = 4, BK = NW * 32, BQ = 32, DCH = D / 8, KK = D / 16, DB = D / 32;
+    // block-sparse: the 128 keys are two mask columns, and a mask row (256
+    // queries) is 8 query tiles
+    static_assert(BK == 2 * FA_SPARSE_BK && FA_SPARSE_BQ == 8 * BQ, "mask granularity");
     constexpr int QT_CH = BQ * DCH, QTB = QT_CH * 16;     // one Q (or dO) tile
     constexpr int VB_CH = BK * DCH;                       // the V block
     constexpr int LPWQ = QT_CH / 64 / NW, LPWV = VB_CH / 64 / NW;
@@ -286,7 +289,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     __shared__ unsigned short qb_list[SPARSE ? kMaxSparseList : 1];
     __shared__ int qb_len;
     int n_sp = 0;                          // block-sparse steps
-    const int qb0 = q_begin / 256;
+    const int qb0 = q_begin / FA_SPARSE_BQ;
     if constexpr (SPARSE) {
         const unsigned char* mk = p.block_mask + (long long)bh * p.n_qb * p.n_kb;
         const int c0 = kt * 2, c1 = kt * 2 + 1;
@@ -301,10 +304,10 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         const int n_list = qb_len;
         n_sp = 8 * n_list;
         if (n_list > 0 && qb0 + (qb_list[n_list - 1] & 0xFFF) == p.n_qb - 1)   // the last block may be partial
-            n_sp -= 8 - (Nq - (p.n_qb - 1) * 256 + BQ - 1) / BQ;
+            n_sp -= 8 - (Nq - (p.n_qb - 1) * FA_SPARSE_BQ + BQ - 1) / BQ;
     }
     // first query of block-sparse step v
-    auto sp_row = [&](int v) { return (qb0 + (qb_list[v >> 3] & 0xFFF)) * 256 + (v & 7) * BQ; };
+    auto sp_row = [&](int v) { return (qb0 + (qb_list[v >> 3] & 0xFFF)) * FA_SPARSE_BQ + (v & 7) * BQ; };
 
     // K^T fragment (B operand of S = Q K^T): K[key][16kk + 8hi .. +7]
     bf16x8 kreg[KK];
@@ -526,6 +529,8 @@ template <int D, bool CAUSAL, bool BAND, bool SPARSE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(BwdParams p) {
     constexpr int NW = 8, BC = 64, BR = NW * 32, DCH = D / 8, KK = D / 16, DB = D / 32;
+    // block-sparse: a mask row is this kernel's query tile, a column its key tile
+    static_assert(BR == FA_SPARSE_BQ && BC == FA_SPARSE_BK, "mask granularity");
     constexpr int TILE_CH = BC * DCH, TB = TILE_CH * 16, LPW = TILE_CH / 64 / NW;
     static_assert(TILE_CH % (64 * NW) == 0, "tile must split evenly over the waves");
 
@@ -805,8 +810,8 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
     p.wl = wl;
     p.wr = wr;
     p.block_mask = block_mask;
-    p.n_qb = (Nq + 255) / 256;       // mask rows: 256 queries
-    p.n_kb = (Nk + 63) / 64;         // mask columns: 64 keys
+    p.n_qb = (Nq + FA_SPARSE_BQ - 1) / FA_SPARSE_BQ;   // mask rows: 256 queries
+    p.n_kb = (Nk + FA_SPARSE_BK - 1) / FA_SPARSE_BK;   // mask columns: 64 keys
     p.n_tiles = 0;
     p.BH = (int)BH;
     p.scale = scale;

@@ -624,10 +624,12 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 
     int j = t_begin;
     if constexpr (BAND) {
-        // Masked first tiles (the band's left edge), serial, until the next
-        // tile is a whole one; then one more serial step if needed so the
-        // pipelined loop starts on stage 0.
-        for (; j + 1 < t_full_lo; ++j) {
+        // Masked first tiles (the band's left edge), serial, until tile j
+        // itself is whole for every row, so every row has seen a key (finite
+        // running max) before the pipelined step, which has no stand-in for
+        // a max of -inf, forms its P; then one more serial step if needed so
+        // the pipelined loop starts on stage 0.
+        for (; j < t_full_lo && j + 1 < n_kt; ++j) {
             FA_TOP(j);
             wave_step_band<D, true>(st, sa, qreg, FA_KS(j + 1), FA_V_STAGE(j), (j + 1) * BC, lo_key, hi_key, sl2,
                                     col, hi, tr_row, tr_dd);
@@ -1068,6 +1070,10 @@ namespace {
 #endif
 constexpr int kWavesBf16 = FA_WAVES_BF16;   // queries per workgroup = 32 * waves
 constexpr int kWavesF32 = 4;
+// A block-sparse mask row covers one workgroup's queries and a mask column
+// one key tile: the public granularity must match the kernel's tiling.
+static_assert(32 * kWavesBf16 == FA_SPARSE_BQ, "block-mask rows must be the bf16 kernel's query tiles");
+static_assert(Bf16Cfg<128, kWavesBf16>::BC == FA_SPARSE_BK, "block-mask columns must be the bf16 kernel's key tiles");
 
 template <int D, bool CAUSAL, bool OUT_BF16>
 hipError_t launch_bf16(const FwdParams& p, int grid, int mode, hipStream_t s) {
@@ -1178,8 +1184,8 @@ fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
     p.wl = window_left < 0 ? -1 : window_left;
     p.wr = window_right < 0 ? -1 : window_right;
     p.block_mask = block_mask;
-    p.n_qb = (int)n_qtiles;          // mask rows: the kernel's 256-query tiles
-    p.n_kb = (Nk + 63) / 64;
+    p.n_qb = (Nq + FA_SPARSE_BQ - 1) / FA_SPARSE_BQ;   // mask rows (= the kernel's query tiles)
+    p.n_kb = (Nk + FA_SPARSE_BK - 1) / FA_SPARSE_BK;   // mask columns (= its key tiles)
     // scale 0 (uniform weights) runs as a tiny positive scale: every scaled
     // score is then below 2^-24 in magnitude and every probability rounds to
     // exactly 1, as with scale 0, while masked (-inf) scores still give 0.

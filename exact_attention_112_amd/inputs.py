@@ -343,3 +343,32 @@ def sample_rows(w: Workload, n: int, seed: int = 7, peaked: np.ndarray | None = 
     if need:
         rows.update(int(x) for x in g.choice(w.Nq, size=min(need, w.Nq), replace=False))
     return np.array(sorted(rows), dtype=np.int32)
+
+
+def tile_rows(w: Workload, per_tile: int, tile: int = 256, seed: int = 17,
+              peaked: np.ndarray | None = None, n_edge: int = 16) -> np.ndarray:
+    """A row table int32 [B*H, R] for row-sampled checks at full size, with
+    rows of its own for every head (b, h) (table row b*H + h): the first and
+    last ``n_edge`` rows, ``per_tile`` seeded-uniform rows inside every
+    ``tile``-row block of queries (so every query tile of a launch is hit, at
+    an offset that differs from head to head), and, when ``peaked`` key
+    positions are given, the ``n_edge`` rows right after the first peaked
+    keys of that head (K/V head h // (H / Hkv)), spread over its sorted list
+    of peaked keys.  Entries may repeat."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    n_tiles = (w.Nq + tile - 1) // tile
+    starts = np.arange(n_tiles) * tile
+    sizes = np.minimum(tile, w.Nq - starts)
+    e = min(n_edge, w.Nq)
+    table = []
+    for bh in range(w.B * w.H):
+        b, h = divmod(bh, w.H)
+        rows = [np.arange(e), np.arange(w.Nq - e, w.Nq)]
+        if peaked is not None:
+            pk = peaked[b, h // (w.H // w.kv_heads)]
+            pick = pk[np.linspace(0, pk.size - 1, n_edge).astype(np.int64)]
+            rows.append(np.minimum(pick + 1, w.Nq - 1))
+        offs = (g.random((per_tile, n_tiles)) * sizes).astype(np.int64)
+        rows.append((starts + offs).reshape(-1))
+        table.append(np.concatenate(rows))
+    return np.stack(table).astype(np.int32)

@@ -80,6 +80,9 @@ class OracleLib:
         f.restype = _c_int
         f.argtypes = ([_c_ptr] * 3 + [_c_i64] * 9 + [_c_int] * 5 + [_c_dbl, _c_int]
                       + [_c_ptr, _c_int, _c_ptr, _c_ptr, _c_int])
+        f2 = self._lib.oracle_attn_fwd_rowtab
+        f2.restype = _c_int
+        f2.argtypes = f.argtypes
         g = self._lib.oracle_attn_probs
         g.restype = _c_int
         g.argtypes = [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_int, _c_int, _c_int,
@@ -107,8 +110,9 @@ class OracleLib:
 
         q, k, v: float32 arrays in the layout's storage shape -- ``BHND`` is
         [B,H,N,d], ``BSND`` is [B,N,H,d].  ``rows``: optional query indices
-        (the same for every (b,h)); default all rows.  ``scale`` is used as
-        given (no default resolution here).
+        (the same for every (b,h)), or a 2-D table [B*H, R] that gives each
+        head (b, h) its own R rows (row b*H + h); default all rows.  ``scale``
+        is used as given (no default resolution here).
         """
         q = np.ascontiguousarray(q, dtype=np.float32)
         k = np.ascontiguousarray(k, dtype=np.float32)
@@ -133,11 +137,14 @@ class OracleLib:
             rows_ptr = None
         else:
             rows_arr = np.ascontiguousarray(rows, dtype=np.int32)
-            R = int(rows_arr.size)
+            if rows_arr.ndim == 2 and rows_arr.shape[0] != B * H:
+                raise ValueError("a row table needs one row of indices per (b, h)")
+            R = int(rows_arr.shape[-1])
             rows_ptr = rows_arr.ctypes.data
         o = np.empty((B, H, R, d), dtype=np.float64)
         lse = np.empty((B, H, R), dtype=np.float64)
-        rc = self._lib.oracle_attn_fwd(
+        fn = self._lib.oracle_attn_fwd_rowtab if rows is not None and rows_arr.ndim == 2 else self._lib.oracle_attn_fwd
+        rc = fn(
             q.ctypes.data, k.ctypes.data, v.ctypes.data,
             *qs, *ks, *ks, B, H, Nq, Nk, d, float(scale), int(bool(causal)),
             rows_ptr, R, o.ctypes.data, lse.ctypes.data, int(n_threads))

@@ -79,29 +79,27 @@ static int one_row(const float* qi, const float* kbh, const float* vbh,
     return nvis;
 }
 
-/*
- * oracle_attn_fwd: O [B,H,R,d] and LSE [B,H,R] in double, where the R rows
- * are `rows[0..n_rows)` (query indices, each in [0,Nq)) or all Nq rows when
- * rows == NULL.  n_threads <= 0 means the OpenMP default.
- * Returns 0 on success, -1 on bad arguments, -2 on allocation failure,
- * -3 if some row has no visible key.
- */
-int oracle_attn_fwd(const float* q, const float* k, const float* v,
-                    int64_t q_sb, int64_t q_sh, int64_t q_sn,
-                    int64_t k_sb, int64_t k_sh, int64_t k_sn,
-                    int64_t v_sb, int64_t v_sh, int64_t v_sn,
-                    int B, int H, int Nq, int Nk, int d,
-                    double scale, int causal,
-                    const int32_t* rows, int n_rows,
-                    double* o, double* lse, int n_threads)
+/* The forward over R rows per (b, h): rows[r] (shared by every head) or,
+ * with rows_per_head, rows[bh * R + r] for head bh = b * H + h; all Nq rows
+ * when rows == NULL. */
+static int attn_fwd_rows(const float* q, const float* k, const float* v,
+                         int64_t q_sb, int64_t q_sh, int64_t q_sn,
+                         int64_t k_sb, int64_t k_sh, int64_t k_sn,
+                         int64_t v_sb, int64_t v_sh, int64_t v_sn,
+                         int B, int H, int Nq, int Nk, int d,
+                         double scale, int causal,
+                         const int32_t* rows, int n_rows, int rows_per_head,
+                         double* o, double* lse, int n_threads)
 {
     if (!q || !k || !v || !o || !lse) return -1;
     if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return -1;
     int R = rows ? n_rows : Nq;
     if (R < 1) return -1;
-    if (rows)
-        for (int r = 0; r < R; ++r)
+    if (rows) {
+        const int64_t n_entries = rows_per_head ? (int64_t)B * H * R : R;
+        for (int64_t r = 0; r < n_entries; ++r)
             if (rows[r] < 0 || rows[r] >= Nq) return -1;
+    }
     if (n_threads <= 0) n_threads = omp_get_max_threads();
 
     int status = 0;
@@ -119,7 +117,7 @@ int oracle_attn_fwd(const float* q, const float* k, const float* v,
             int64_t bh = t / R;
             int r = (int)(t % R);
             int b = (int)(bh / H), h = (int)(bh % H);
-            int i = rows ? rows[r] : r;
+            int i = rows ? rows[(rows_per_head ? bh * R : 0) + r] : r;
             const float* qi = q + b * q_sb + h * q_sh + (int64_t)i * q_sn;
             const float* kbh = k + b * k_sb + h * k_sh;
             const float* vbh = v + b * v_sb + h * v_sh;
@@ -133,6 +131,45 @@ int oracle_attn_fwd(const float* q, const float* k, const float* v,
         free(s);
     }
     return status;
+}
+
+/*
+ * oracle_attn_fwd: O [B,H,R,d] and LSE [B,H,R] in double, where the R rows
+ * are `rows[0..n_rows)` (query indices, each in [0,Nq)) or all Nq rows when
+ * rows == NULL.  n_threads <= 0 means the OpenMP default.
+ * Returns 0 on success, -1 on bad arguments, -2 on allocation failure,
+ * -3 if some row has no visible key.
+ */
+int oracle_attn_fwd(const float* q, const float* k, const float* v,
+                    int64_t q_sb, int64_t q_sh, int64_t q_sn,
+                    int64_t k_sb, int64_t k_sh, int64_t k_sn,
+                    int64_t v_sb, int64_t v_sh, int64_t v_sn,
+                    int B, int H, int Nq, int Nk, int d,
+                    double scale, int causal,
+                    const int32_t* rows, int n_rows,
+                    double* o, double* lse, int n_threads)
+{
+    return attn_fwd_rows(q, k, v, q_sb, q_sh, q_sn, k_sb, k_sh, k_sn, v_sb, v_sh, v_sn,
+                         B, H, Nq, Nk, d, scale, causal, rows, n_rows, 0, o, lse, n_threads);
+}
+
+/*
+ * oracle_attn_fwd_rowtab: as oracle_attn_fwd, with a row table of its own
+ * for every (b, h): rows [B*H][n_rows], entry [b*H + h][r] is the query
+ * index of output row r of head (b, h).
+ */
+int oracle_attn_fwd_rowtab(const float* q, const float* k, const float* v,
+                           int64_t q_sb, int64_t q_sh, int64_t q_sn,
+                           int64_t k_sb, int64_t k_sh, int64_t k_sn,
+                           int64_t v_sb, int64_t v_sh, int64_t v_sn,
+                           int B, int H, int Nq, int Nk, int d,
+                           double scale, int causal,
+                           const int32_t* rows, int n_rows,
+                           double* o, double* lse, int n_threads)
+{
+    if (!rows) return -1;
+    return attn_fwd_rows(q, k, v, q_sb, q_sh, q_sn, k_sb, k_sh, k_sn, v_sb, v_sh, v_sn,
+                         B, H, Nq, Nk, d, scale, causal, rows, n_rows, 1, o, lse, n_threads);
 }
 
 /*

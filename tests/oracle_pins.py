@@ -269,6 +269,22 @@ def pin_rows_subset(lib):
             assert np.array_equal(of[:, :, rows], os_) and np.array_equal(lf[:, :, rows], ls)
 
 
+def pin_row_table(lib):
+    """A row table (rows of their own for each head) returns, for every head,
+    exactly its rows of the full run, in the table's order."""
+    for layout in ("BHND", "BSND"):
+        q, k, v = _rand_case(901, 2, 3, 20, 23, 8)
+        q, k, v = (_to_layout(x, layout) for x in (q, k, v))
+        g = _rng(902)
+        table = np.stack([g.permutation(20)[:5] for _ in range(6)]).astype(np.int32)
+        for causal in (False, True):
+            of, lf = lib.attn_fwd(q, k, v, scale=0.3, causal=causal, layout=layout)
+            ot, lt = lib.attn_fwd(q, k, v, scale=0.3, causal=causal, layout=layout, rows=table)
+            for bh in range(6):
+                b, h = divmod(bh, 3)
+                assert np.array_equal(of[b, h, table[bh]], ot[b, h]) and np.array_equal(lf[b, h, table[bh]], lt[b, h])
+
+
 # ---------------------------------------------------------------------------
 # worked examples
 
@@ -315,5 +331,5 @@ def pin_stress_classes(lib):
 ALL_PINS = [
     pin_torch_sdpa, pin_decimal_bruteforce, pin_all_ones, pin_uniform, pin_dominant_key,
     pin_single_key_and_causal_row0, pin_key_shift, pin_permutation, pin_probs_normalised,
-    pin_rows_subset, pin_worked_examples, pin_stress_classes,
+    pin_rows_subset, pin_row_table, pin_worked_examples, pin_stress_classes,
 ]

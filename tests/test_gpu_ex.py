@@ -71,6 +71,11 @@ CASES = {
     "band_right_of_query": BASE.scaled(B=1, H=2, Nq=260, Nk=400, window=(0, -1)),
     "swa_gqa_many_tiles": PRE.scaled(H=4, Hkv=2, Nq=1500, Nk=1500, window=(256, -1)),
     "band_noncausal_many_tiles": BASE.scaled(B=1, H=2, Nq=1100, Nk=1300, window=(300, 200)),
+    # the last workgroup's last row starts its band at the first key of a
+    # tile that follows an even number of masked left-edge tiles: the
+    # pipelined loop must not form P of a tile before that row has seen a key
+    "swa_left_edge_parity_1089": PRE.scaled(H=2, Nq=1089, Nk=1089, window=(512, -1)),
+    "swa_left_edge_parity_4161": PRE.scaled(H=2, Nq=4161, Nk=4161, window=(1024, -1)),
 }
 
 

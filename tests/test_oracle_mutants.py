@@ -25,7 +25,8 @@ MUTANTS = {
     "min_instead_of_max": ("if (s[j] > m) m = s[j];\n    /* pass 2", "if (s[j] < m) m = s[j];\n    /* pass 2"),
     "dot_product_index": ("dot += (double)qi[c] * (double)kj[c];\n        s[j] = scale * dot;",
                           "dot += (double)qi[c] * (double)kj[0];\n        s[j] = scale * dot;"),
-    "query_row_off_by_one": ("int i = rows ? rows[r] : r;", "int i = rows ? rows[r] : (r + 1) % Nq;"),
+    "query_row_off_by_one": ("int i = rows ? rows[(rows_per_head ? bh * R : 0) + r] : r;",
+                             "int i = rows ? rows[(rows_per_head ? bh * R : 0) + r] : (r + 1) % Nq;"),
     "sum_misses_first_key": ("        l += p;\n", "        if (j > 0) l += p;\n"),
     "head_stride_swapped": ("const float* kbh = k + b * k_sb + h * k_sh;",
                             "const float* kbh = k + b * k_sb + h * k_sn;"),

@@ -17,3 +17,8 @@ def test_oracle_rejects_bad_arguments(oracle_lib):
         oracle_lib.attn_fwd(q, q, q, scale=1.0, rows=np.array([4], np.int32))
     with pytest.raises(RuntimeError):
         oracle_lib.attn_fwd(q, q, q, scale=1.0, rows=np.array([-1], np.int32))
+    table = np.array([[0, 4]], np.int32)
+    with pytest.raises(RuntimeError):
+        oracle_lib.attn_fwd(q, q, q, scale=1.0, rows=table)
+    with pytest.raises(ValueError):
+        oracle_lib.attn_fwd(q, q, q, scale=1.0, rows=np.zeros((2, 1), np.int32))
