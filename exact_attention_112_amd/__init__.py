@@ -34,7 +34,8 @@ FA_BF16, FA_F32 = 0, 1
 LAYOUTS = {"BHND": FA_BHND, "BSND": FA_BSND}
 
 # the symbols include/fa355.h declares
-EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_sparse", "fa_bwd", "fa_bwd_ex", "fa_bwd_sparse", "fa_decode", "fa_decode_workspace_bytes", "fa_status_str",
+EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_sparse", "fa_bwd", "fa_bwd_ex", "fa_bwd_sparse", "fa_decode",
+           "fa_decode_workspace_bytes", "fa_decode_noalloc", "fa_status_str",
            "fa_abi_version")
 ABI_VERSION = 1
 
@@ -79,6 +80,9 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.fa_decode.restype = ctypes.c_int
     lib.fa_decode.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.c_size_t] + [ctypes.c_int] * 7 + [ctypes.c_float]
                               + [ctypes.c_int] * 3 + [ctypes.c_void_p])
+    lib.fa_decode_noalloc.restype = ctypes.c_int
+    lib.fa_decode_noalloc.argtypes = ([ctypes.c_void_p] * 7 + [ctypes.c_int] * 7 + [ctypes.c_float]
+                                      + [ctypes.c_int] * 3 + [ctypes.c_void_p])
     lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_decode_workspace_bytes.argtypes = [ctypes.c_int] * 6
     lib.fa_bwd.restype = ctypes.c_int
@@ -330,6 +334,21 @@ def fa_decode(q: int, k_cache: int, v_cache: int, block_tables: int, seq_lens: i
     return int(load().fa_decode(q, k_cache, v_cache, block_tables, seq_lens, o, lse or None, workspace,
                                 int(workspace_bytes), B, H, Hkv, Nq, d, block_size, max_blocks, float(scale),
                                 int(causal), int(in_dtype), int(o_dtype), stream or None))
+
+
+def fa_decode_noalloc(q: int, k_cache: int, v_cache: int, block_tables: int, seq_lens: int, o: int,
+                      lse: int | None, B: int, H: int, Hkv: int, Nq: int, d: int, block_size: int, max_blocks: int,
+                      scale: float, causal: int, in_dtype: int, o_dtype: int, stream: int | None) -> int:
+    """The C entry point without a workspace (the library's fixed device
+    array holds the chunk partials); raw device addresses; returns the
+    fa_status."""
+    return int(load().fa_decode_noalloc(q, k_cache, v_cache, block_tables, seq_lens, o, lse or None, B, H, Hkv,
+                                        Nq, d, block_size, max_blocks, float(scale), int(causal), int(in_dtype),
+                                        int(o_dtype), stream or None))
+
+
+# fa_decode_noalloc's limit on the chunk partials (include/fa355.h)
+DECODE_NOALLOC_MAX_WORKSPACE = 64 << 20
 
 
 def fa_decode_workspace_bytes(B: int, H: int, Hkv: int, Nq: int, d: int, max_seq_len: int) -> int:

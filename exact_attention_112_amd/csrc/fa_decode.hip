@@ -36,6 +36,8 @@
 #include <stdint.h>
 #include <math.h>
 
+#include <atomic>
+
 #include "fa355.h"
 #include "fa_common.h"
 
@@ -327,19 +329,78 @@ extern "C" size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int Nq, int d
     return (size_t)((long long)B * H * Nq * S * (d + 1) * 4);
 }
 
+namespace {
+
+// The decode call behind fa_decode and fa_decode_noalloc.  With workspace ==
+// nullptr the chunk partials go to this device's fixed scratch array (looked
+// up only after every argument has been validated).
+fa_status decode_impl(const void* q, const void* k_cache, const void* v_cache, const int* block_tables,
+                      const int* seq_lens, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                      int B, int H, int Hkv, int Nq, int d, int block_size, int max_blocks, float scale,
+                      int causal, int in_dtype, int o_dtype, void* stream);
+
+}  // namespace
+
 extern "C" fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* block_tables,
                                const int* seq_lens, void* o, float* lse, void* workspace, size_t workspace_bytes,
                                int B, int H, int Hkv, int Nq, int d, int block_size, int max_blocks, float scale,
                                int causal, int in_dtype, int o_dtype, void* stream) {
+    if (!workspace) return FA_ERR_INVALID_ARG;
+    return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, o, lse, workspace, workspace_bytes, B, H, Hkv,
+                       Nq, d, block_size, max_blocks, scale, causal, in_dtype, o_dtype, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace: the chunk partials live in a file-scope
+// device array of fixed size.  Each GPU the library runs on holds its own
+// copy until the process ends; host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device (kept per device after
+// the first call there), never through the array's name.
+
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)FA_DECODE_NOALLOC_MAX_WORKSPACE;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// This device's address of `scratch` (nullptr on a HIP error).
+void* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr) return ptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    return ptr;
+}
+
+}  // namespace
+
+extern "C" fa_status fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                       const int* block_tables, const int* seq_lens, void* o, float* lse, int B, int H,
+                                       int Hkv, int Nq, int d, int block_size, int max_blocks, float scale, int causal,
+                                       int in_dtype, int o_dtype, void* stream) {
+    return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, o, lse, nullptr, 0, B, H, Hkv, Nq, d,
+                       block_size, max_blocks, scale, causal, in_dtype, o_dtype, stream);
+}
+
+namespace {
+
+fa_status decode_impl(const void* q, const void* k_cache, const void* v_cache, const int* block_tables,
+                      const int* seq_lens, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                      int B, int H, int Hkv, int Nq, int d, int block_size, int max_blocks, float scale,
+                      int causal, int in_dtype, int o_dtype, void* stream) {
     // ---- validation: no HIP call before it passes
-    if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !o || !workspace) return FA_ERR_INVALID_ARG;
+    if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !o) return FA_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || Hkv < 1 || Nq < 1 || d < 1 || max_blocks < 1) return FA_ERR_INVALID_ARG;
     if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
     if (block_size < 16 || block_size > (1 << 20) || (block_size & (block_size - 1)) != 0) return FA_ERR_INVALID_ARG;
     if (in_dtype != FA_BF16 && in_dtype != FA_F32) return FA_ERR_INVALID_ARG;
     if (o_dtype != FA_BF16 && o_dtype != FA_F32) return FA_ERR_INVALID_ARG;
     if (!aligned_d(q, 16) || !aligned_d(k_cache, 16) || !aligned_d(v_cache, 16) || !aligned_d(o, 16) ||
-        !aligned_d(workspace, 16) || !aligned_d(block_tables, 4) || !aligned_d(seq_lens, 4))
+        (workspace && !aligned_d(workspace, 16)) || !aligned_d(block_tables, 4) || !aligned_d(seq_lens, 4))
         return FA_ERR_INVALID_ARG;
     if (lse && !aligned_d(lse, 4)) return FA_ERR_INVALID_ARG;
     if (scale != scale || fabsf(scale) == INFINITY) return FA_ERR_INVALID_ARG;
@@ -348,7 +409,12 @@ extern "C" fa_status fa_decode(const void* q, const void* k_cache, const void* v
     const long long max_len = (long long)max_blocks * block_size;
     if (max_len > INT32_MAX / 2) return FA_ERR_UNSUPPORTED;
     const size_t need = fa_decode_workspace_bytes(B, H, Hkv, Nq, d, (int)max_len);
-    if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+    if (workspace) {
+        if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+    } else {
+        // the fixed scratch array: sizes whose partials do not fit are refused
+        if (need > kScratchBytes) return FA_ERR_UNSUPPORTED;
+    }
     const int S = decode_splits(B, H, Hkv, Nq, (int)max_len);
     const long long G = (long long)(H / Hkv) * Nq;
     const long long n_rt = (G + 31) / 32;
@@ -356,6 +422,10 @@ extern "C" fa_status fa_decode(const void* q, const void* k_cache, const void* v
     const long long rows = (long long)B * H * Nq;
     if (items > INT32_MAX || (items + 3) / 4 > INT32_MAX || (rows + 3) / 4 > INT32_MAX) return FA_ERR_UNSUPPORTED;
 
+    if (!workspace) {
+        workspace = scratch_for_current_device();
+        if (!workspace) return FA_ERR_HIP;
+    }
     if (scale < 0.f) scale = 1.0f / sqrtf((float)d);
     DecodeParams p;
     p.q = q; p.k_cache = k_cache; p.v_cache = v_cache; p.block_tables = block_tables; p.seq_lens = seq_lens;
@@ -392,3 +462,5 @@ extern "C" fa_status fa_decode(const void* q, const void* k_cache, const void* v
     }
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
+
+}  // namespace

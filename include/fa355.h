@@ -287,6 +287,34 @@ FA355_API fa_status fa_decode(const void* q, const void* k_cache, const void* v_
  * block_size); 0 for invalid sizes. */
 FA355_API size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int Nq, int d, int max_seq_len);
 
+/* Largest workspace fa_decode_noalloc can stand in for (bytes). */
+#define FA_DECODE_NOALLOC_MAX_WORKSPACE (64u << 20)
+
+/*
+ * fa_decode_noalloc -- fa_decode without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * that may not call hipMalloc).  Same operation, arguments (less workspace
+ * and workspace_bytes), kernels and results as fa_decode.  The chunk
+ * partials go to a fixed device array of FA_DECODE_NOALLOC_MAX_WORKSPACE
+ * bytes inside the library: each GPU it runs on holds its own copy until the
+ * process ends; the first call on a device looks up that device's copy
+ * (hipGetSymbolAddress, with the device current).  Nothing is allocated: no
+ * hipMalloc, no hipFree, no allocating library call.
+ *
+ * Every call on one GPU shares that GPU's array, and the array keeps the last
+ * call's partials (every partial a call reads, it first writes).  Calls that
+ * overlap on one GPU (concurrent streams, or several host threads) race on it
+ * and must be ordered by the caller.
+ *
+ * Errors: as fa_decode; FA_ERR_UNSUPPORTED when the partials of these sizes
+ * (fa_decode_workspace_bytes) exceed FA_DECODE_NOALLOC_MAX_WORKSPACE;
+ * FA_ERR_HIP if the array's address cannot be looked up.
+ */
+FA355_API fa_status fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int* block_tables, const int* seq_lens, void* o, float* lse, int B, int H,
+                                      int Hkv, int Nq, int d, int block_size, int max_blocks, float scale,
+                                      int causal, int in_dtype, int o_dtype, void* stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 FA355_API const char* fa_status_str(int status);
 
