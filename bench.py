@@ -25,8 +25,9 @@ throughput in TFLOP/s (4*B*H*Nq*Nk*d, halved for causal) and:
   Atlas 800), for context only.
 
 ``--workload all`` runs the five forward workloads one after another (30
-timed launches after 5 warmup launches; 10 after 2 for the 128K context),
-prints one line each and, with ``--out PATH``, writes them to a JSON file.
+timed launches after 5 warmup launches and at least one second of warmup;
+10 after 2 for the 128K context), prints one line each and, with ``--out
+PATH``, writes them to a JSON file.
 
 With ``--pass bwd`` one step is one fa_bwd call (D = rowsum(dO*O), the dK/dV
 kernel and the dQ kernel) on the workload, given O and LSE from one forward
@@ -449,12 +450,15 @@ def bench_decode(args, w):
     return 0
 
 
-def bench_attention(args, w, steps: int, warmup: int, with_cpu: bool):
+def bench_attention(args, w, steps: int, warmup: int, with_cpu: bool, min_warmup_s: float = 0.0):
     """Time ``steps`` calls of the forward (or, with args.which == "bwd", the
     backward) pass on workload ``w`` after ``warmup`` untimed calls; returns
-    the JSON record (None on a non-finite output).  Each launch is bracketed
-    by HIP events on the stream the kernels run on; ``ms_per_step`` is the
-    mean over the timed launches (back to back, no cache flush)."""
+    the JSON record (None on a non-finite output).  With ``min_warmup_s`` the
+    warmup continues past ``warmup`` calls until that much time has passed
+    (short kernels: the GPU clock ramps up over tens of milliseconds).  Each
+    launch is bracketed by HIP events on the stream the kernels run on;
+    ``ms_per_step`` is the mean over the timed launches (back to back, no
+    cache flush)."""
     import numpy as np
     import torch
     import exact_attention_112_amd as fa
@@ -502,6 +506,12 @@ def bench_attention(args, w, steps: int, warmup: int, with_cpu: bool):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    if min_warmup_s > 0:
+        t_w = time.perf_counter()
+        while time.perf_counter() - t_w < min_warmup_s:
+            for _ in range(20):
+                step()
+            torch.cuda.synchronize()
     stream = torch.cuda.current_stream()        # the stream fa.fwd / fa.bwd launch on
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     print(f"bench: timing {steps} steps", file=sys.stderr, flush=True)
@@ -638,7 +648,7 @@ def main(argv=None):
         for name in names:
             w = I.WORKLOADS[name]
             steps, warmup = (10, 2) if w.Nq >= 65536 else (30, 5)
-            rec = bench_attention(args, w, steps, warmup, with_cpu=not args.no_cpu_baseline)
+            rec = bench_attention(args, w, steps, warmup, with_cpu=not args.no_cpu_baseline, min_warmup_s=1.0)
             if rec is None:
                 return 1
             print(json.dumps(rec), flush=True)

@@ -260,10 +260,11 @@ __device__ __forceinline__ void update_max(RowState<D>& st, float mt2) {
 
 // The same step with its instruction order fixed by hand (every group ends
 // in a scheduling fence): phase A issues each K fragment read three MFMAs
-// ahead of its use and runs two exponentials per score MFMA; its last three
-// groups already fetch the first V^T fragments; phase B issues each V^T
-// fragment three MFMAs ahead and takes the row max of tile j+1 in small
-// chunks once its scores have left the matrix core.
+// ahead of its use and runs one or two exponentials per score MFMA; its last
+// three groups already fetch the first V^T fragments; phase B issues each
+// V^T fragment three MFMAs ahead, finishes the exponentials and takes the
+// row max of tile j+1 in small chunks once its scores have left the matrix
+// core.
 template <int D>
 __device__ __forceinline__ void wave_step_sw(RowState<D>& st, const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
                                              const bf16x8 (&qreg)[D / 16], const u32x4* __restrict__ ks,
@@ -272,14 +273,15 @@ __device__ __forceinline__ void wave_step_sw(RowState<D>& st, const f32x16 (&s_c
     constexpr int DCH = D / 8, DB = D / 32;
     constexpr int NA = 2 * (D / 16);      // score MFMAs
     constexpr int NB = 4 * DB;            // P V MFMAs
-    // exponential pairs (16 per tile): PA of them in phase A, PPM per score
-    // MFMA; the rest in the first groups of phase B, before the P V MFMAs
-    // that need them (d = 128: 12 + 4, which spreads the vector work more
-    // evenly over the two phases)
-    constexpr int PA = D == 128 ? 12 : 16;
-    constexpr int PPM = PA / NA > 0 ? PA / NA : 1;
+    // exponentials (32 per lane and tile), element by element: EA of them
+    // spread evenly over the NA groups of phase A, the rest over the first GB
+    // groups of phase B, each before the P V MFMA that needs it (d = 128:
+    // 22 + 10, one or two per score MFMA and one per P V MFMA, so that no
+    // group's vector work exceeds what the other wave's MFMA hides)
+    constexpr int EA = D == 128 ? 22 : 32;
+    constexpr int GB = D == 128 ? 10 : 1;
     constexpr int CPS = NB == 16 ? 1 : 2; // max chunks per P V MFMA
-    constexpr int MS = 16 - PA > 2 ? 16 - PA : 2;   // first group of the max chunks
+    constexpr int MS = D == 128 ? 4 : 2;   // first group of the max chunks
     auto kread = [&](int i) -> bf16x8 {
         const int kk = i >> 1, kb = i & 1, row = kb * 32 + col;
         return __builtin_bit_cast(bf16x8, ks[row * DCH + k_swz<D>(row, 2 * kk + hi)]);
@@ -296,6 +298,18 @@ __device__ __forceinline__ void wave_step_sw(RowState<D>& st, const f32x16 (&s_c
     };
     const float nm = -st.m;
     unsigned pk[2][8];
+    float ev[32];
+    // element e: score s_cur[e / 16][e % 16]; odd elements close a pair
+    auto elem = [&](int e) {
+        const int b = e >> 4, r = e & 15;
+        ev[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][r], sl2, nm));
+        if (e & 1) {
+            st.l1 += ev[e];
+            pk[b][r >> 1] = pack_bf16x2(ev[e - 1], ev[e]);
+        } else {
+            st.l0 += ev[e];
+        }
+    };
     bf16x8 kf[4], vf[4];
 #pragma unroll
     for (int i = 0; i < 3; ++i) kf[i] = kread(i);
@@ -309,16 +323,7 @@ __device__ __forceinline__ void wave_step_sw(RowState<D>& st, const f32x16 (&s_c
         s_nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], qreg[i >> 1], i < 2 ? f32x16{} : s_nxt[kb],
                                                             0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < PPM; ++e) {
-            const int pr = i * PPM + e, b = pr >> 3, jj = pr & 7;
-            if (pr < PA) {
-                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][2 * jj], sl2, nm));
-                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][2 * jj + 1], sl2, nm));
-                st.l0 += e0;
-                st.l1 += e1;
-                pk[b][jj] = pack_bf16x2(e0, e1);
-            }
-        }
+        for (int e = (EA * i) / NA; e < (EA * (i + 1)) / NA; ++e) elem(e);
         __builtin_amdgcn_sched_barrier(0);
     }
     // phase B
@@ -330,13 +335,9 @@ __device__ __forceinline__ void wave_step_sw(RowState<D>& st, const f32x16 (&s_c
         const bf16x8 pb = __builtin_bit_cast(
             bf16x8, (u32x4){pk[kb][4 * u + 0], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]});
         st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 3], pb, st.oacc[db], 0, 0, 0);
-        if (PA + i < 16) {
-            const int pr = PA + i, b = pr >> 3, jj = pr & 7;
-            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][2 * jj], sl2, nm));
-            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][2 * jj + 1], sl2, nm));
-            st.l0 += e0;
-            st.l1 += e1;
-            pk[b][jj] = pack_bf16x2(e0, e1);
+        if (i < GB) {
+#pragma unroll
+            for (int e = EA + ((32 - EA) * i) / GB; e < EA + ((32 - EA) * (i + 1)) / GB; ++e) elem(e);
         }
 #pragma unroll
         for (int cc = 0; cc < CPS; ++cc) {
