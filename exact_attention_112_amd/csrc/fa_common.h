@@ -27,14 +27,21 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Workgroup id -> (batch*head, tile of rows).  Workgroups are dispatched round
 // robin over the 8 XCDs; when B*H is a multiple of 8, each XCD gets a
 // contiguous block of whole heads so one head's K/V stays in one XCD's L2.
-// Causal: heaviest (last) query tiles first.  A bijection in all cases.
+// Causal: heaviest (last) query tiles first -- across the XCD's heads, or,
+// with head_major (long sequences, at least as many tiles per head as an XCD
+// has CUs), one head after another, so the tiles an XCD runs at once belong
+// to one head and walk its keys together through L2.  A bijection in all
+// cases.
 __device__ __forceinline__ void tile_of_block(int bid, int n_tiles, int BH, bool causal,
-                                              int& bh, int& qt) {
+                                              int& bh, int& qt, bool head_major = false) {
     if ((BH & 7) == 0) {
         const int hpx = BH >> 3;
         const int xcd = bid & 7;
         const int s = bid >> 3;
-        if (causal) {
+        if (causal && head_major) {
+            bh = xcd * hpx + s / n_tiles;
+            qt = n_tiles - 1 - s % n_tiles;
+        } else if (causal) {
             qt = n_tiles - 1 - s / hpx;
             bh = xcd * hpx + s % hpx;
         } else {

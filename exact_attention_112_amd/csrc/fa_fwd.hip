@@ -432,7 +432,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     const int hi = lane >> 5;
 
     int bh, qt;
-    tile_of_block(__builtin_amdgcn_workgroup_id_x(), p.n_qtiles, p.BH, CAUSAL, bh, qt);
+    // long causal sequences: one head at a time per XCD (32 CUs each)
+    tile_of_block(__builtin_amdgcn_workgroup_id_x(), p.n_qtiles, p.BH, CAUSAL, bh, qt, p.n_qtiles >= 32);
     const int b = bh / p.H;
     const int h = bh - b * p.H;
 
