@@ -607,6 +607,9 @@ def main(argv=None):
                     help="time the forward pass (default) or the backward pass")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
+    ap.add_argument("--min-warmup-s", type=float, default=0.0, metavar="SECONDS",
+                    help="keep warming up past --warmup calls until this much time has passed (short "
+                         "kernels: the clock ramps up over tens of milliseconds); --workload all uses 1")
     ap.add_argument("--out", default=None, metavar="PATH",
                     help="with --workload all: also write every record to this JSON file")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -648,7 +651,8 @@ def main(argv=None):
         for name in names:
             w = I.WORKLOADS[name]
             steps, warmup = (10, 2) if w.Nq >= 65536 else (30, 5)
-            rec = bench_attention(args, w, steps, warmup, with_cpu=not args.no_cpu_baseline, min_warmup_s=1.0)
+            rec = bench_attention(args, w, steps, warmup, with_cpu=not args.no_cpu_baseline,
+                                  min_warmup_s=max(1.0, args.min_warmup_s))
             if rec is None:
                 return 1
             print(json.dumps(rec), flush=True)
@@ -658,7 +662,7 @@ def main(argv=None):
                 json.dump({"records": records}, f, indent=1)
         return 0
     rec = bench_attention(args, I.WORKLOADS[args.workload], args.steps, args.warmup,
-                          with_cpu=not args.no_cpu_baseline)
+                          with_cpu=not args.no_cpu_baseline, min_warmup_s=args.min_warmup_s)
     if rec is None:
         return 1
     print(json.dumps(rec), flush=True)
