@@ -114,6 +114,10 @@ __device__ __forceinline__ void rows_times_frag(f32x16 (&acc)[NKB], const bf16x8
     }
 }
 
+// Four consecutive floats from LDS.  (Read through a __restrict__ pointer
+// like the tiles: the compiler then adds no wait for tile loads in flight.)
+__device__ __forceinline__ float4 lds_f4(const float* __restrict__ p) { return *(const float4*)p; }
+
 // acc[db] += T^T X for a tile T of 32*NKB rows in LDS (read transposed) and X
 // the packed bf16 operand of those rows in the 32x32 output layout of a
 // previous product (pk[kb][j] = rows (kb*32 + 2j, +1) of the lane's column,
@@ -121,7 +125,7 @@ __device__ __forceinline__ void rows_times_frag(f32x16 (&acc)[NKB], const bf16x8
 // group u are rows 16u + hi*4 + 0..3, slots 4..7 rows 16u + 8 + hi*4 + 0..3.
 template <int D, int NKB>
 __device__ __forceinline__ void tr_times_packed(f32x16 (&acc)[D / 32], const unsigned (&pk)[NKB][8],
-                                                const lds_char* tile, int tr_row, int tr_dd) {
+                                                const lds_char* __restrict__ tile, int tr_row, int tr_dd) {
     constexpr int DB = D / 32;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -227,9 +231,18 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     constexpr int LPWQ = QT_CH / 64 / NW, LPWV = VB_CH / 64 / NW;
     static_assert(QT_CH % (64 * NW) == 0 && VB_CH % (64 * NW) == 0, "tiles must split evenly");
 
-    // V block, then Q stages 0, 1, then dO stages 0, 1
-    __shared__ u32x4 smem[VB_CH + 4 * QT_CH];
-    __shared__ __attribute__((aligned(16))) float stat[2][2][BQ];   // [stage][lse*log2e, D][query]
+    // LDS: the V block, Q stages 0 and 1, dO stages 0 and 1, the two stages'
+    // statistics ([stage][lse*log2e, D][query]) and, block-sparse, the list of
+    // query blocks and its length.  One LDS array for all of it: with a second
+    // LDS variable in the kernel the compiler makes every read of a tile wait
+    // for the tile loads still in flight (those of the next step, into the
+    // other stage).
+    constexpr int STAT_CH = 2 * 2 * BQ * 4 / 16;
+    constexpr int LIST_CH = SPARSE ? kMaxSparseList * 2 / 16 + 1 : 0;
+    __shared__ u32x4 smem[VB_CH + 4 * QT_CH + STAT_CH + LIST_CH];
+    float(*const stat)[2][BQ] = reinterpret_cast<float(*)[2][BQ]>(smem + VB_CH + 4 * QT_CH);
+    unsigned short* const qb_list = reinterpret_cast<unsigned short*>(smem + VB_CH + 4 * QT_CH + STAT_CH);
+    int* const qb_len = reinterpret_cast<int*>(qb_list + kMaxSparseList);
 
     const int tid = __builtin_amdgcn_workitem_id_x();
     const int lane = tid & 63;
@@ -286,8 +299,6 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     // bit 14 + c if column c is marked); a wave skips the blocks that leave
     // its own column off and sees the others whole (apart from the causal
     // diagonal and rows past Nq)
-    __shared__ unsigned short qb_list[SPARSE ? kMaxSparseList : 1];
-    __shared__ int qb_len;
     int n_sp = 0;                          // block-sparse steps
     const int qb0 = q_begin / FA_SPARSE_BQ;
     if constexpr (SPARSE) {
@@ -298,10 +309,10 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
                 const unsigned char* mr = mk + (long long)(qb0 + t) * p.n_kb;
                 return (mr[c0] != 0 ? 0x4000u : 0u) | (c1 < p.n_kb && mr[c1] != 0 ? 0x8000u : 0u);
             });
-            if (lane == 0) qb_len = cnt;
+            if (lane == 0) *qb_len = cnt;
         }
         __syncthreads();
-        const int n_list = qb_len;
+        const int n_list = *qb_len;
         n_sp = 8 * n_list;
         if (n_list > 0 && qb0 + (qb_list[n_list - 1] & 0xFFF) == p.n_qb - 1)   // the last block may be partial
             n_sp -= 8 - (Nq - (p.n_qb - 1) * FA_SPARSE_BQ + BQ - 1) / BQ;
@@ -354,13 +365,15 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         st_lse = INFINITY;
         st_dl = 0.f;
         if (wave == 0 && lane < BQ && i < Nq) {
-            st_lse = p.lse[stat_row + i] * kLog2e;
+            st_lse = p.lse[stat_row + i];
             st_dl = p.delta[stat_row + i];
         }
     };
+    // (the loads above are first used here, after the step's wait for all
+    // loads: using them earlier would wait for the tile loads issued before)
     auto store_stat = [&](int t) {
         if (wave == 0 && lane < BQ) {
-            stat[t & 1][0][lane] = st_lse;
+            stat[t & 1][0][lane] = st_lse * kLog2e;
             stat[t & 1][1][lane] = st_dl;
         }
     };
@@ -456,7 +469,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             // it, in a uniform branch
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float4 l4 = *(const float4*)&stat[t & 1][0][g * 8 + hi * 4];
+                const float4 l4 = lds_f4(&stat[t & 1][0][g * 8 + hi * 4]);
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -473,7 +486,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             }
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float4 d4 = *(const float4*)&stat[t & 1][1][g * 8 + hi * 4];
+                const float4 d4 = lds_f4(&stat[t & 1][1][g * 8 + hi * 4]);
                 const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
                 float se[4];
 #pragma unroll
@@ -489,8 +502,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             // spills here)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float4 l4 = *(const float4*)&stat[t & 1][0][g * 8 + hi * 4];
-                const float4 d4 = *(const float4*)&stat[t & 1][1][g * 8 + hi * 4];
+                const float4 l4 = lds_f4(&stat[t & 1][0][g * 8 + hi * 4]);
+                const float4 d4 = lds_f4(&stat[t & 1][1][g * 8 + hi * 4]);
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
                 float pe[4], se[4];
 #pragma unroll
@@ -534,8 +547,14 @@ void fa_bwd_dq_kernel(BwdParams p) {
     constexpr int TILE_CH = BC * DCH, TB = TILE_CH * 16, LPW = TILE_CH / 64 / NW;
     static_assert(TILE_CH % (64 * NW) == 0, "tile must split evenly over the waves");
 
-    // K stages 0, 1 then V stages 0, 1
-    __shared__ u32x4 smem[4 * TILE_CH];
+    // LDS: K stages 0, 1, V stages 0, 1 and, block-sparse, the list of key
+    // tiles and its length, in one LDS array (with a second LDS variable the
+    // compiler makes every read of a tile wait for the loads in flight into
+    // the other stage)
+    constexpr int LIST_CH = SPARSE ? kMaxSparseList * 2 / 16 + 1 : 0;
+    __shared__ u32x4 smem[4 * TILE_CH + LIST_CH];
+    unsigned short* const tile_list = reinterpret_cast<unsigned short*>(smem + 4 * TILE_CH);
+    int* const list_len = reinterpret_cast<int*>(tile_list + kMaxSparseList);
 
     const int tid = __builtin_amdgcn_workitem_id_x();
     const int lane = tid & 63;
@@ -592,16 +611,14 @@ void fa_bwd_dq_kernel(BwdParams p) {
     // Block-sparse: the workgroup's 256 queries are one mask row; the steps
     // run over the sorted list of the key tiles it marks (a marked tile is
     // seen whole, apart from the causal diagonal and the ragged last tile)
-    __shared__ unsigned short tile_list[SPARSE ? kMaxSparseList : 1];
-    __shared__ int list_len;
     if constexpr (SPARSE) {
         const unsigned char* mrow = p.block_mask + ((long long)bh * p.n_qb + qt) * p.n_kb;
         if (wave == 0) {
             const int cnt = build_list(tile_list, n_kt, lane, [&](int t) { return mrow[t] != 0 ? 1u : 0u; });
-            if (lane == 0) list_len = cnt;
+            if (lane == 0) *list_len = cnt;
         }
         __syncthreads();
-        n_kt = list_len;
+        n_kt = *list_len;
     }
 
     bf16x8 qreg[KK], greg[KK];

@@ -422,8 +422,14 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     constexpr int BC = C::BC, BR = C::BR, DCH = C::DCH, TILE_CH = C::TILE_CH, TB = C::TILE_BYTES;
     constexpr int LPW = C::LPW, KK = D / 16, DB = D / 32;
 
-    // K stages 0, 1 then V stages 0, 1; [TILE_CH] 16-byte chunks each
-    __shared__ u32x4 smem[4 * TILE_CH];
+    // LDS: K stages 0, 1, V stages 0, 1 ([TILE_CH] 16-byte chunks each) and,
+    // block-sparse, the list of key tiles and its length, in one LDS array
+    // (with a second LDS variable the compiler makes every read of a tile
+    // wait for the loads in flight into the other stage)
+    constexpr int LIST_CH = SPARSE ? kMaxSparseTiles * 2 / 16 + 1 : 0;
+    __shared__ u32x4 smem[4 * TILE_CH + LIST_CH];
+    unsigned short* const tile_list = reinterpret_cast<unsigned short*>(smem + 4 * TILE_CH);
+    int* const list_len = reinterpret_cast<int*>(tile_list + kMaxSparseTiles);
 
     const int tid = __builtin_amdgcn_workitem_id_x();
     const int lane = tid & 63;
@@ -495,8 +501,6 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // tiles; "tile" v below is then list entry v.  The tiles a wave or the
     // whole workgroup sees in full are a prefix of the list (the list is
     // sorted and only the diagonal / last tiles need a mask).
-    __shared__ unsigned short tile_list[SPARSE ? kMaxSparseTiles : 1];
-    __shared__ int list_len;
     if constexpr (SPARSE) {
         const unsigned char* mrow = p.block_mask + ((long long)bh * p.n_qb + qt) * p.n_kb;
         if (wave == 0) {
@@ -510,10 +514,10 @@ void fa_fwd_bf16_kernel(FwdParams p) {
                 if (on) tile_list[pos] = (unsigned short)t;
                 count += __builtin_popcountll(bal);
             }
-            if (lane == 0) list_len = count;
+            if (lane == 0) *list_len = count;
         }
         __syncthreads();
-        const int n_list = list_len;
+        const int n_list = *list_len;
         int v_full = 0, v_wave = 0;
         for (int base = 0; base < n_list; base += 64) {
             const int v = base + lane;
