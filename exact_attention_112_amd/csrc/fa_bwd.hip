@@ -219,6 +219,174 @@ __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(BwdParams p) {
 //   tile against key col;
 //   dK^T, dV^T accumulators: acc[db][r] = d index db*32 + (r/4)*8 + hi*4 + r%4
 //   of key col.
+//
+// One step of a wave: the 32 queries of the tile in the Q and dO stages
+// against the wave's 32 keys, in four chains of MFMAs with the instruction
+// order fixed by hand (each group ends in a scheduling fence), every LDS
+// operand read issued two or three MFMAs ahead of its use:
+//   A: S = Q K^T (Q rows from LDS, K^T in registers);
+//   B: dP = dO V^T (dO rows and V rows from LDS), and under it the
+//      probabilities P = exp2(S scale log2e - LSE log2e), element by element;
+//   C: dV^T += dO^T P (dO read transposed), and under it dS = P (dP - D);
+//   D: dK^T += Q^T dS (Q read transposed).
+// MASK: element e (query off(e) = (e/4)*8 + hi*4 + e%4 of the tile) is kept
+// only if vlo <= (e/4)*8 + e%4, and with UPPER also <= vhi (the bounds
+// already less hi*4).
+//   qt, gt: this step's Q and dO stages; vb: the V block; st: this step's
+//   statistics (LSE log2e of the 32 queries, then D).
+#ifndef DKDV_QA
+#define DKDV_QA 3
+#endif
+#ifndef DKDV_GB
+#define DKDV_GB 2
+#endif
+#ifndef DKDV_TC
+#define DKDV_TC 2
+#endif
+// Per-lane LDS byte offsets of a dK/dV step's reads.  The swizzles only flip
+// bits inside a row's chunk field, so one XOR with a constant (and an
+// immediate offset) turns each into the address of every read of the step:
+//   qa: row col, chunk hi of a Q or dO tile; read kk at qa ^ 32kk
+//   va: row vrow, chunk hi of the V block; read kk at va ^ 32kk
+//   ta0, ta1: transposed reads of rows tr_row and tr_row + 8, d values from
+//        tr_dd; MFMA (u, db) at (ta ^ 64db) + 16u rows
+// (valid for tile bases that are multiples of 256 bytes)
+struct DkdvOffsets {
+    unsigned qa, va, ta0, ta1;
+};
+template <int D>
+__device__ __forceinline__ DkdvOffsets dkdv_offsets(int col, int hi, int vrow, int tr_row, int tr_dd) {
+    constexpr int RB = D * 2;
+    const int c0 = tr_dd >> 3, w = (tr_dd & 7) * 2;
+    DkdvOffsets o;
+    o.qa = col * RB + kv_swz<D>(col, hi) * 16;
+    o.va = vrow * RB + k_swz<D>(vrow, hi) * 16;
+    o.ta0 = tr_row * RB + kv_swz<D>(tr_row, c0) * 16 + w;
+    o.ta1 = (tr_row + 8) * RB + kv_swz<D>(tr_row + 8, c0) * 16 + w;
+    return o;
+}
+__device__ __forceinline__ unsigned lds_addr(const lds_char* p) { return (unsigned)(uintptr_t)p; }
+
+template <int D, bool MASK, bool UPPER>
+__device__ __forceinline__ void dkdv_step(f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], const bf16x8 (&kreg)[D / 16],
+                                          const lds_char* qt, const lds_char* gt, const lds_char* vb,
+                                          const float* __restrict__ st, DkdvOffsets o, int hi, float sl2, int vlo,
+                                          int vhi) {
+    constexpr int KK = D / 16, DB = D / 32, NT = 2 * DB, RB = D * 2;
+    // the offsets pass through an empty asm statement: the compiler then
+    // forms each read's address next to the read, every step, instead of
+    // keeping all of them in registers across the loop
+    asm volatile("" : "+v"(o.qa), "+v"(o.va), "+v"(o.ta0), "+v"(o.ta1));
+    const unsigned qb = lds_addr(qt) + o.qa, gb = lds_addr(gt) + o.qa, vbb = lds_addr(vb) + o.va;
+    const unsigned tq0 = lds_addr(qt) + o.ta0, tq1 = lds_addr(qt) + o.ta1;
+    const unsigned tg0 = lds_addr(gt) + o.ta0, tg1 = lds_addr(gt) + o.ta1;
+    typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+    auto rd = [](unsigned a) { return __builtin_bit_cast(bf16x8, *(lds_u32x4*)(uintptr_t)a); };
+    auto qread = [&](int kk) { return rd(qb ^ (32u * kk)); };
+    auto gread = [&](int kk) { return rd(gb ^ (32u * kk)); };
+    auto vread = [&](int kk) { return rd(vbb ^ (32u * kk)); };
+    // A operand of MFMA i = u*DB + db of a transposed product (tile Q or dO)
+    auto trread = [&](bool q, int i) -> bf16x8 {
+        const int u = i / DB, db = i % DB;
+        const unsigned a0 = ((q ? tq0 : tg0) ^ (64u * db)) + 16u * u * RB;
+        const unsigned a1 = ((q ? tq1 : tg1) ^ (64u * db)) + 16u * u * RB;
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a0);
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a1);
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto vis = [&](int e) {
+        const int c = (e >> 2) * 8 + (e & 3);
+        return !MASK || (c >= vlo && (!UPPER || c <= vhi));
+    };
+
+    // read-ahead distances (MFMAs) of the Q rows, of the dO and V rows, and
+    // of the transposed reads
+    constexpr int QA = DKDV_QA, GB = DKDV_GB, TC = DKDV_TC;
+    f32x16 s, dp;      // S, then P in place, then dS in place
+    unsigned pkp[8], pks[8];
+    bf16x8 qf[QA + 1], gf[GB + 1], vf[GB + 1], tf[TC + 1];
+    float4 l4[2], d4[2];
+
+    // A: S chain; Q reads QA MFMAs ahead, then the first dO / V reads for B
+#pragma unroll
+    for (int i = 0; i < QA; ++i) qf[i] = qread(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        if (kk + QA < KK) qf[(kk + QA) % (QA + 1)] = qread(kk + QA);
+        if (kk == KK - 3) l4[0] = lds_f4(st + 0 * 8 + hi * 4);
+        if (kk >= KK - GB) {
+            const int j = kk - (KK - GB);
+            gf[j] = gread(j);
+            vf[j] = vread(j);
+        }
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[kk % (QA + 1)], kreg[kk], kk == 0 ? f32x16{} : s, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // B: dP chain, dO / V reads GB MFMAs ahead; the 16 exponentials over
+    // groups 1 .. KK-1 (group 0 would wait for the last S MFMA)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        if (kk + GB < KK) {
+            gf[(kk + GB) % (GB + 1)] = gread(kk + GB);
+            vf[(kk + GB) % (GB + 1)] = vread(kk + GB);
+        }
+        if (kk >= KK - TC) tf[kk - (KK - TC)] = trread(false, kk - (KK - TC));
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gf[kk % (GB + 1)], vf[kk % (GB + 1)], kk == 0 ? f32x16{} : dp,
+                                                     0, 0, 0);
+        if (kk >= 1) {
+#pragma unroll
+            for (int e = 16 * (kk - 1) / (KK - 1); e < 16 * kk / (KK - 1); ++e) {
+                const int g = e >> 2;
+                if ((e & 3) == 0 && g + 1 < 4) l4[(g + 1) & 1] = lds_f4(st + (g + 1) * 8 + hi * 4);
+                const float4 l = l4[g & 1];
+                const float lv = (e & 3) == 0 ? l.x : (e & 3) == 1 ? l.y : (e & 3) == 2 ? l.z : l.w;
+                float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sl2, -lv));
+                if (!vis(e)) pe = 0.f;
+                s[e] = pe;
+                if (e & 1) pkp[e >> 1] = pack_bf16x2(s[e - 1], pe);
+            }
+        }
+        if (kk == KK - 1) d4[0] = lds_f4(st + 32 + 0 * 8 + hi * 4);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // C: dV chain, transposed reads TC MFMAs ahead (read n = 0 .. 2NT-1:
+    // dO^T for C, then Q^T for D, into tf[n % (TC+1)]); dS over groups
+    // 1 .. NT-1
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const int n = i + TC;
+        if (n < NT) tf[n % (TC + 1)] = trread(false, n);
+        else tf[n % (TC + 1)] = trread(true, n - NT);
+        const int u = i / DB, db = i % DB;
+        const bf16x8 pb =
+            __builtin_bit_cast(bf16x8, (u32x4){pkp[4 * u + 0], pkp[4 * u + 1], pkp[4 * u + 2], pkp[4 * u + 3]});
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[i % (TC + 1)], pb, dv[db], 0, 0, 0);
+        if (i >= 1) {
+#pragma unroll
+            for (int e = 16 * (i - 1) / (NT - 1); e < 16 * i / (NT - 1); ++e) {
+                const int g = e >> 2;
+                if ((e & 3) == 0 && g + 1 < 4) d4[(g + 1) & 1] = lds_f4(st + 32 + (g + 1) * 8 + hi * 4);
+                const float4 dd = d4[g & 1];
+                const float dv_ = (e & 3) == 0 ? dd.x : (e & 3) == 1 ? dd.y : (e & 3) == 2 ? dd.z : dd.w;
+                s[e] = s[e] * (dp[e] - dv_);
+                if (e & 1) pks[e >> 1] = pack_bf16x2(s[e - 1], s[e]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // D: dK chain, Q^T reads TC MFMAs ahead
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        if (i + TC < NT) tf[(NT + i + TC) % (TC + 1)] = trread(true, i + TC);
+        const int u = i / DB, db = i % DB;
+        const bf16x8 sb =
+            __builtin_bit_cast(bf16x8, (u32x4){pks[4 * u + 0], pks[4 * u + 1], pks[4 * u + 2], pks[4 * u + 3]});
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[(NT + i) % (TC + 1)], sb, dk[db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <int D, bool CAUSAL, bool BAND, bool GQA, bool SPARSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
@@ -239,7 +407,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     // other stage).
     constexpr int STAT_CH = 2 * 2 * BQ * 4 / 16;
     constexpr int LIST_CH = SPARSE ? kMaxSparseList * 2 / 16 + 1 : 0;
-    __shared__ u32x4 smem[VB_CH + 4 * QT_CH + STAT_CH + LIST_CH];
+    __shared__ __attribute__((aligned(256))) u32x4 smem[VB_CH + 4 * QT_CH + STAT_CH + LIST_CH];
     float(*const stat)[2][BQ] = reinterpret_cast<float(*)[2][BQ]>(smem + VB_CH + 4 * QT_CH);
     unsigned short* const qb_list = reinterpret_cast<unsigned short*>(smem + VB_CH + 4 * QT_CH + STAT_CH);
     int* const qb_len = reinterpret_cast<int*>(qb_list + kMaxSparseList);
@@ -386,6 +554,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     const int tr_row = hi * 4 + (ti >> 2);
     const int tr_dd = 16 * (tg & 1) + 4 * (ti & 3);
     const float sl2 = p.scale_log2;
+    const DkdvOffsets offs = dkdv_offsets<D>(col, hi, vrow, tr_row, tr_dd);
 
     // steps t = 0 .. n_vt - 1, each issuing the next one's loads; with
     // grouped heads the query heads of the group run one after the other
@@ -442,86 +611,26 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             if (CAUSAL && i0 + BQ - 1 < kw0) continue;
         }
 
-        const u32x4* qs = (const u32x4*)(qst + (t & 1) * QTB);
-        const u32x4* gs = (const u32x4*)(gst + (t & 1) * QTB);
-        f32x16 s[1], dp[1];
-        rows_times_frag<D, 1, 2>(s, kreg, qs, col, hi);
-        // dP = dO V^T: A rows from the dO stage, B = V^T fragment from the V block
-        {
-            const u32x4* vb = (const u32x4*)vblk;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const u32x4 a = gs[col * DCH + kv_swz<D>(col, 2 * kk + hi)];
-                const u32x4 bv = vb[vrow * DCH + k_swz<D>(vrow, 2 * kk + hi)];
-                const f32x16 c = kk == 0 ? f32x16{} : dp[0];
-                dp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                __builtin_bit_cast(bf16x8, bv), c, 0, 0, 0);
-            }
-        }
-        // P = exp2(s*scale*log2e - lse2), dS = P (dP - D); masked pairs get 0
-        // (rows past Nq have P = 0 from their statistics)
+        // P = exp2(s*scale*log2e - lse2), dS = P (dP - D); pairs outside the
+        // causal mask or the band get 0, on the tiles that cross an edge (rows
+        // past Nq have P = 0 from their statistics)
+        const lds_char* const qt = qst + (t & 1) * QTB;
+        const lds_char* const gt = gst + (t & 1) * QTB;
+        const float* const st = &stat[t & 1][0][0];
         bool masked = CAUSAL && i0 < kw0 + 31;
         if constexpr (BAND)
             masked = masked || (p.wl >= 0 && i0 + BQ - 1 - p.wl > kw0) || (p.wr >= 0 && i0 + p.wr < kw0 + 31);
-        unsigned pkp[1][8], pks[1][8];
-        if constexpr (BAND) {
-            // the band's edges: the per-element mask only on the tiles that need
-            // it, in a uniform branch
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const float4 l4 = lds_f4(&stat[t & 1][0][g * 8 + hi * 4]);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    s[0][4 * g + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][4 * g + e], sl2, -lv[e]));
-            }
-            if (masked) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int qi = i0 + (r >> 2) * 8 + hi * 4 + (r & 3);
-                    const bool vis = (!CAUSAL || key <= qi) && (p.wl < 0 || key >= qi - p.wl) &&
-                                     (p.wr < 0 || key <= qi + p.wr);
-                    s[0][r] = vis ? s[0][r] : 0.f;
-                }
-            }
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const float4 d4 = lds_f4(&stat[t & 1][1][g * 8 + hi * 4]);
-                const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
-                float se[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) se[e] = s[0][4 * g + e] * (dp[0][4 * g + e] - dvv[e]);
-                pkp[0][2 * g + 0] = pack_bf16x2(s[0][4 * g + 0], s[0][4 * g + 1]);
-                pkp[0][2 * g + 1] = pack_bf16x2(s[0][4 * g + 2], s[0][4 * g + 3]);
-                pks[0][2 * g + 0] = pack_bf16x2(se[0], se[1]);
-                pks[0][2 * g + 1] = pack_bf16x2(se[2], se[3]);
-            }
+        if constexpr (CAUSAL || BAND) {
+            // element bounds of dkdv_step (the lane's query offset less hi*4),
+            // open on the tiles that cross no edge
+            const int base = key - i0 - hi * 4;
+            int vlo = CAUSAL && masked ? base : -(1 << 30), vhi = 1 << 30;
+            if (BAND && masked && p.wr >= 0) vlo = max(vlo, (int)max((long long)base - p.wr, -(1LL << 30)));
+            if (BAND && masked && p.wl >= 0) vhi = (int)min((long long)base + p.wl, 1LL << 30);
+            dkdv_step<D, true, BAND>(dk, dv, kreg, qt, gt, vblk, st, offs, hi, sl2, vlo, vhi);
         } else {
-            // (written this way the compiler applies the causal mask's selects
-            // to every tile, but keeps every register; the branch form above
-            // spills here)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const float4 l4 = lds_f4(&stat[t & 1][0][g * 8 + hi * 4]);
-                const float4 d4 = lds_f4(&stat[t & 1][1][g * 8 + hi * 4]);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
-                float pe[4], se[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * g + e;
-                    float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][r], sl2, -lv[e]));
-                    if (masked) pr = key <= i0 + g * 8 + hi * 4 + e ? pr : 0.f;   // the causal diagonal
-                    pe[e] = pr;
-                    se[e] = pr * (dp[0][r] - dvv[e]);
-                }
-                pkp[0][2 * g + 0] = pack_bf16x2(pe[0], pe[1]);
-                pkp[0][2 * g + 1] = pack_bf16x2(pe[2], pe[3]);
-                pks[0][2 * g + 0] = pack_bf16x2(se[0], se[1]);
-                pks[0][2 * g + 1] = pack_bf16x2(se[2], se[3]);
-            }
+            dkdv_step<D, false, false>(dk, dv, kreg, qt, gt, vblk, st, offs, hi, sl2, 0, 0);
         }
-        tr_times_packed<D, 1>(dv, pkp, gst + (t & 1) * QTB, tr_row, tr_dd);
-        tr_times_packed<D, 1>(dk, pks, qst + (t & 1) * QTB, tr_row, tr_dd);
     }
 #undef FA_ISSUE_QG
 
