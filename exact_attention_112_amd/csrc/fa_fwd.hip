@@ -53,6 +53,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "fa355.h"
 #include "fa_common.h"
@@ -264,9 +265,11 @@ __device__ __forceinline__ void update_max(RowState<D>& st, float mt2) {
 // three groups already fetch the first V^T fragments; phase B issues each
 // V^T fragment three MFMAs ahead, finishes the exponentials and takes the
 // row max of tile j+1 in small chunks once its scores have left the matrix
-// core.
-template <int D>
-__device__ __forceinline__ void wave_step_sw(RowState<D>& st, const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+// core.  BOUNDARY: tile j+1 is the first tile of the next query tile (the
+// persistent kernel): the running max is left alone and the next tile's
+// scaled max is returned.
+template <int D, bool BOUNDARY = false>
+__device__ __forceinline__ float wave_step_sw(RowState<D>& st, const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
                                              const bf16x8 (&qreg)[D / 16], const u32x4* __restrict__ ks,
                                              const lds_char* __restrict__ vs, float sl2, int col, int hi,
                                              int tr_row, int tr_dd) {
@@ -357,7 +360,9 @@ __device__ __forceinline__ void wave_step_sw(RowState<D>& st, const f32x16 (&s_c
         __builtin_amdgcn_sched_barrier(0);
     }
     st.xl = xl_new;
+    if constexpr (BOUNDARY) return mt2;   // s_nxt starts the next query tile: no rescale
     update_max(st, mt2);
+    return 0.f;
 }
 
 // The same step without the overlap, for the few masked tiles at the end:
@@ -718,6 +723,228 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 
 
 // ---------------------------------------------------------------------------
+// Persistent form of the plain non-causal kernel, for Nk a multiple of 128
+// (every key tile whole, an even number of them).
+//
+// gridDim.x workgroups (a multiple of 8, about one per CU) each take the
+// query tiles bid, bid + G, bid + 2G, ... of the ordinary kernel's
+// workgroup order (so an XCD keeps the heads tile_of_block gives it) and run
+// their key tiles as one stream: the loads issued at the top of a query
+// tile's last two steps already fetch the next query tile's Q (into an LDS
+// buffer) and its first K and V tiles, and its last step computes the next
+// query tile's first scores while it finishes P V of its own last tile.  A
+// query tile thus starts without waiting for its Q or its first tiles, and
+// ends without a serial step; O and LSE are stored between the two.
+template <int D, int NW, bool OUT_BF16>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_bf16_persist(FwdParams p, int n_items) {
+    using C = Bf16Cfg<D, NW>;
+    constexpr int BC = C::BC, BR = C::BR, DCH = C::DCH, TILE_CH = C::TILE_CH, TB = C::TILE_BYTES;
+    constexpr int LPW = C::LPW, KK = D / 16, DB = D / 32;
+    constexpr int Q_CH = BR * DCH, LPQ = Q_CH / 64 / NW;   // the Q tile in LDS, loads per wave
+    static_assert(Q_CH % (64 * NW) == 0, "Q tile must split evenly over the waves");
+
+    // LDS: K stages 0, 1, V stages 0, 1, then the Q tile (one LDS array)
+    __shared__ u32x4 smem[4 * TILE_CH + Q_CH];
+    lds_char* const lds = (lds_char*)smem;
+    lds_char* const qbuf = lds + 4 * TB;
+
+    const int tid = __builtin_amdgcn_workitem_id_x();
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31;
+    const int hi = lane >> 5;
+    const int G = __builtin_amdgcn_readfirstlane((int)gridDim.x);
+    const int Nq = p.Nq, Nk = p.Nk;
+    const int n_kt = Nk / BC;                     // even, >= 2
+    const unsigned rb = (unsigned)(p.k_sn * 2);   // K/V row bytes
+    const unsigned qrb = (unsigned)(p.q_sn * 2);  // Q/O row bytes (in elements x 2)
+    const int my_row = wave * 32 + col;           // this lane's query row in the tile
+
+    // the query tile of work item `it` (a workgroup id of the ordinary kernel):
+    // its (batch, head) and first row; addresses are formed when needed
+    struct Item {
+        int bh, q0;
+    };
+    auto item_of = [&](int it) {
+        Item r;
+        int qt;
+        tile_of_block(it, p.n_qtiles, p.BH, false, r.bh, qt);
+        r.q0 = qt * BR;
+        return r;
+    };
+    const unsigned long long v_minus_k =
+        (unsigned long long)((const char*)p.v - (const char*)p.k);   // V's offset from K (same strides)
+    auto k_addr = [&](const Item& it) {
+        const int b = it.bh / p.H, h = it.bh - b * p.H, hk = h / p.group;
+        return to_sgpr((unsigned long long)((const __bf16*)p.k + (long long)b * p.k_sb + (long long)hk * p.k_sh));
+    };
+    auto q_addr = [&](const Item& it) {
+        const int b = it.bh / p.H, h = it.bh - b * p.H;
+        return to_sgpr((unsigned long long)((const __bf16*)p.q + (long long)b * p.q_sb + (long long)h * p.q_sh +
+                                            (long long)it.q0 * p.q_sn));
+    };
+
+    unsigned ld_koff, ld_voff, ld_qoff;   // byte offsets inside a tile (load round 0)
+    {
+        const int row = wave * (64 / DCH) + lane / DCH, ch = lane % DCH;
+        ld_koff = row * rb + k_swz<D>(row, ch) * 16;
+        ld_voff = row * rb + v_swz<D>(row, ch) * 16;
+        ld_qoff = row * qrb + k_swz<D>(row, ch) * 16;
+    }
+    const unsigned long long tile_bytes = (unsigned long long)BC * rb;
+    lds_char* const ldst = lds + wave * 1024;         // this wave's rows of load round 0 in a stage
+    lds_char* const ldq = qbuf + wave * 1024;
+#define FA_K_STAGE(t) (lds + ((t) & 1) * TB)
+#define FA_V_STAGE(t) (lds + (2 + ((t) & 1)) * TB)
+// (kb: the K base of the query tile's head, a scalar; V is at kb + v_minus_k)
+#define FA_ISSUE_K(kb, t) issue_tile<LPW, DCH, BC, NW>((kb) + (unsigned long long)(t) * tile_bytes, rb, ld_koff, \
+                                                       ldst + ((t) & 1) * TB, BC, wave, lane)
+#define FA_ISSUE_V(kb, t) issue_tile<LPW, DCH, BC, NW>((kb) + v_minus_k + (unsigned long long)(t) * tile_bytes, rb, \
+                                                       ld_voff, ldst + (2 + ((t) & 1)) * TB, BC, wave, lane)
+#define FA_ISSUE_Q(qb, q0) issue_tile<LPQ, DCH, BR, NW>((qb), qrb, ld_qoff, ldq, Nq - (q0), wave, lane)
+    const int tg = lane >> 4, ti = lane & 15;
+    const int tr_row = hi * 4 + (ti >> 2);
+    const int tr_dd = 16 * (tg & 1) + 4 * (ti & 3);
+    const float sl2 = p.scale_log2;
+
+    // Q fragment of this lane's row from the LDS Q tile (rows past Nq hold
+    // copies of row Nq-1: finite, not stored)
+    bf16x8 qreg[KK];
+    auto load_q = [&]() {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            qreg[kk] = __builtin_bit_cast(
+                bf16x8, *(const u32x4*)(qbuf + my_row * (D * 2) + k_swz<D>(my_row, 2 * kk + hi) * 16));
+    };
+    RowState<D> st;
+    auto reset = [&](float m) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st.oacc[db][r] = 0.f;
+        st.m = m;
+        st.l0 = 0.f;
+        st.l1 = 0.f;
+        st.dl = 0.f;
+    };
+    // O = acc / (l + dl) and LSE of the finished query tile
+    auto store_out = [&](const Item& it) {
+        const float l_tot = pair_sum(st.l0 + st.l1);
+        const float dl_tot = pair_sum(st.dl);
+        const int hi_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5;
+        const int q = it.q0 + my_row;
+        if (q < Nq) {
+            const float inv = 1.0f / (l_tot + dl_tot);
+            const int b = it.bh / p.H, h = it.bh - b * p.H;
+            char* obase = (char*)p.o;
+            const long long orow = (long long)b * p.q_sb + (long long)h * p.q_sh + (long long)q * p.q_sn;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int dd = db * 32 + g * 8 + hi_e * 4;
+                    const float o0 = st.oacc[db][4 * g + 0] * inv, o1 = st.oacc[db][4 * g + 1] * inv;
+                    const float o2 = st.oacc[db][4 * g + 2] * inv, o3 = st.oacc[db][4 * g + 3] * inv;
+                    if constexpr (OUT_BF16) {
+                        u32x2 w = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+                        *(u32x2*)(obase + (orow + dd) * 2) = w;
+                    } else {
+                        *(float4*)(obase + (orow + dd) * 4) = make_float4(o0, o1, o2, o3);
+                    }
+                }
+            if (p.lse && hi_e == 0) p.lse[(long long)it.bh * Nq + q] = (st.m + __builtin_amdgcn_logf(l_tot)) * kLn2;
+        }
+    };
+
+    int item = __builtin_amdgcn_workgroup_id_x();
+    if (item >= n_items) return;                  // (the host launches at most n_items workgroups)
+    Item cur = item_of(item);
+    unsigned long long k_cur = k_addr(cur);
+    f32x16 sa[2], sb[2];
+    // the first query tile: Q, K tiles 0 and 1, V tile 0, then its first scores
+    FA_ISSUE_Q(q_addr(cur), cur.q0);
+    FA_ISSUE_K(k_cur, 0);
+    FA_ISSUE_V(k_cur, 0);
+    FA_ISSUE_K(k_cur, 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    load_q();
+    qk_tile<D>(sa, qreg, (const u32x4*)FA_K_STAGE(0), col, hi);
+    st.xl = -INFINITY;
+    reset(tile_max_scaled(sa, sl2, st.xl));
+
+    for (;;) {
+        const int nxt = item + G;
+        const bool has_nxt = nxt < n_items;
+        const Item next = item_of(has_nxt ? nxt : item);
+        const unsigned long long k_nxt = k_addr(next), q_nxt = q_addr(next);
+        // Step j (top: K tile j+1 and V tile j have landed for every wave,
+        // and every wave is done with step j-1) refills the stages step j-1
+        // read (K tile j+2, V tile j+1, of this query tile or the next);
+        // then computes P_j, O += P_j V_j and the scores of tile j+1.
+#define FA_TOP(j)                                                                  \
+    do {                                                                           \
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                           \
+        __syncthreads();                                                           \
+        if ((j) + 2 < n_kt) FA_ISSUE_K(k_cur, (j) + 2);                            \
+        else if (has_nxt) FA_ISSUE_K(k_nxt, (j) + 2 - n_kt);                       \
+        if ((j) + 1 < n_kt) FA_ISSUE_V(k_cur, (j) + 1);                            \
+        else if (has_nxt) FA_ISSUE_V(k_nxt, 0);                                    \
+        if ((j) + 2 == n_kt && has_nxt) FA_ISSUE_Q(q_nxt, next.q0);               \
+    } while (0)
+        // (n_kt is even, so inside the loop every tile to load is this query tile's)
+#define FA_TOP_IN(j)                                      \
+    do {                                                  \
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  \
+        __syncthreads();                                  \
+        FA_ISSUE_K(k_cur, (j) + 2);                       \
+        FA_ISSUE_V(k_cur, (j) + 1);                       \
+    } while (0)
+        int j = 0;
+        for (; j + 2 < n_kt; j += 2) {
+            FA_TOP_IN(j);
+            wave_step_sw<D>(st, sa, sb, qreg, (const u32x4*)FA_K_STAGE(j + 1), FA_V_STAGE(j), sl2, col, hi,
+                            tr_row, tr_dd);
+            FA_TOP_IN(j + 1);
+            wave_step_sw<D>(st, sb, sa, qreg, (const u32x4*)FA_K_STAGE(j + 2), FA_V_STAGE(j + 1), sl2, col, hi,
+                            tr_row, tr_dd);
+        }
+#undef FA_TOP_IN
+        // j = n_kt - 2: P_j and the scores of the last tile (the Q loads
+        // into the LDS buffer are safe: every wave read its fragment of this
+        // query tile before its first barrier)
+        FA_TOP(j);
+        wave_step_sw<D>(st, sa, sb, qreg, (const u32x4*)FA_K_STAGE(j + 1), FA_V_STAGE(j), sl2, col, hi, tr_row,
+                        tr_dd);
+        ++j;
+        // j = n_kt - 1: P of the last tile; the next query tile's Q and its
+        // K tile 0 landed at this top
+        FA_TOP(j);
+        if (!has_nxt) {
+            wave_step_serial<D, false, false>(st, sb, qreg, nullptr, FA_V_STAGE(j), 0, 0, Nk, sl2, col, hi, tr_row,
+                                              tr_dd);
+            store_out(cur);
+            break;
+        }
+        load_q();
+        const float m_next = wave_step_sw<D, true>(st, sb, sa, qreg, (const u32x4*)FA_K_STAGE(0), FA_V_STAGE(j),
+                                                   sl2, col, hi, tr_row, tr_dd);
+        store_out(cur);
+        reset(m_next);
+        item = nxt;
+        cur = next;
+        k_cur = k_nxt;
+#undef FA_TOP
+    }
+#undef FA_K_STAGE
+#undef FA_V_STAGE
+#undef FA_ISSUE_K
+#undef FA_ISSUE_V
+#undef FA_ISSUE_Q
+}
+
+// ---------------------------------------------------------------------------
 // Short-key kernel (bf16, at most 32*NKB <= 128 keys, no band or block mask).
 //
 // With this few keys a query row costs little arithmetic and the pass is
@@ -1071,6 +1298,9 @@ using namespace fa355;
 
 namespace {
 
+#ifndef FA_PERSIST
+#define FA_PERSIST 1
+#endif
 #ifndef FA_WAVES_BF16
 #define FA_WAVES_BF16 8
 #endif
@@ -1093,6 +1323,27 @@ hipError_t launch_bf16(const FwdParams& p, int grid, int mode, hipStream_t s) {
         hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, kWavesBf16, CAUSAL, OUT_BF16, kPlain>), dim3(grid),
                            dim3(kWavesBf16 * 64), 0, s, p);
     return hipGetLastError();
+}
+
+// Persistent non-causal kernel: `grid` workgroups over n_items query tiles.
+template <int D, bool OUT_BF16>
+hipError_t launch_persist(const FwdParams& p, int grid, int n_items, hipStream_t s) {
+    hipLaunchKernelGGL((fa_fwd_bf16_persist<D, kWavesBf16, OUT_BF16>), dim3(grid), dim3(kWavesBf16 * 64), 0, s, p,
+                       n_items);
+    return hipGetLastError();
+}
+
+// CUs of the current device (cached per device; 0 if unknown).
+int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 // Short-key kernel: NKB = ceil(Nk / 32) blocks of 32 keys.
@@ -1223,6 +1474,16 @@ fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
     }
     if (in_dtype == FA_BF16) {
         const bool ob = o_dtype == FA_BF16;
+        // Plain non-causal attention over whole key tiles (an even number),
+        // with at least two query tiles per CU: the persistent kernel, one
+        // workgroup per CU (a multiple of 8, for the XCD map)
+        const int ncu = cu_count() & ~7;
+        if (FA_PERSIST && mode == kPlain && !c && Nk % 128 == 0 && ncu > 0 && grid >= 2LL * ncu) {
+            const int g = ncu, ni = (int)grid;
+            if (d == 128) err = ob ? launch_persist<128, true>(p, g, ni, s) : launch_persist<128, false>(p, g, ni, s);
+            else err = ob ? launch_persist<64, true>(p, g, ni, s) : launch_persist<64, false>(p, g, ni, s);
+            return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+        }
         const int g = (int)grid;
         if (d == 128) {
             err = c ? (ob ? launch_bf16<128, true, true>(p, g, mode, s) : launch_bf16<128, true, false>(p, g, mode, s))
