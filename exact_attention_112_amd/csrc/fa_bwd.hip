@@ -68,25 +68,6 @@ struct BwdParams {
 // Most 64-key tiles (dQ) or 256-query blocks (dK/dV) a block-sparse call lists.
 constexpr int kMaxSparseList = 4096;
 
-// Sorted list of the indices t < n whose entry row[t] is nonzero, built by
-// one wave (ballot + mbcnt, 64 entries a round) into LDS; returns the count.
-// `extra(t)` is ORed into the stored entry (bits above the index).
-template <typename F>
-__device__ __forceinline__ int build_list(unsigned short* list, int n, int lane, F entry) {
-    int count = 0;
-    for (int base = 0; base < n; base += 64) {
-        const int t = base + lane;
-        const unsigned e = t < n ? entry(t) : 0u;
-        const bool on = e != 0u;
-        const unsigned long long bal = __builtin_amdgcn_ballot_w64(on);
-        const int pos = count + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
-        if (on) list[pos] = (unsigned short)((unsigned)t | (e & 0xF000u));
-        count += __builtin_popcountll(bal);
-    }
-    return count;
-}
-
 // Swizzle selector for the LDS tiles: 0 = k_swz (rows read only with
 // ds_read_b128), 2 = kv_swz (rows read both ways).
 template <int D, int SWZ>
@@ -461,6 +442,10 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         }
     }
     const int n_qt = q_begin <= q_last ? (q_last - q_begin) / BQ + 1 : 0;
+    // K^T fragment (B operand of S = Q K^T): K[key][16kk + 8hi .. +7]
+    // (loaded before the block-sparse list is built, so the two latencies overlap)
+    bf16x8 kreg[KK];
+    load_frag<D>(kreg, (const __bf16*)p.k + koff, p.k_sn, key, Nk, hi);
     // Block-sparse: the block's 128 keys are two mask columns (waves 0-1 and
     // 2-3); the steps run over the 32-row tiles of the sorted list of the
     // 256-query blocks that mark either column (entry: block - first block,
@@ -488,9 +473,6 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     // first query of block-sparse step v
     auto sp_row = [&](int v) { return (qb0 + (qb_list[v >> 3] & 0xFFF)) * FA_SPARSE_BQ + (v & 7) * BQ; };
 
-    // K^T fragment (B operand of S = Q K^T): K[key][16kk + 8hi .. +7]
-    bf16x8 kreg[KK];
-    load_frag<D>(kreg, (const __bf16*)p.k + koff, p.k_sn, key, Nk, hi);
 
     f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -717,6 +699,15 @@ void fa_bwd_dq_kernel(BwdParams p) {
         tw_hi = (CAUSAL ? min(n_kt, (q_w0 + 31) / BC + 1) : n_kt) - 1;
     }
     const int n_kt_wave = tw_hi + 1;      // no band: the wave's tiles are 0 .. n_kt_wave - 1
+    // (loaded before the block-sparse list is built, so the two latencies overlap)
+    bf16x8 qreg[KK], greg[KK];
+    load_frag<D>(qreg, (const __bf16*)p.q + qoff, p.q_sn, q, Nq, hi);
+    load_frag<D>(greg, (const __bf16*)p.dout + qoff, p.q_sn, q, Nq, hi);
+    float lse2 = 0.f, dlt = 0.f;
+    if (q < Nq) {
+        lse2 = p.lse[(long long)bh * Nq + q] * kLog2e;
+        dlt = p.delta[(long long)bh * Nq + q];
+    }
     // Block-sparse: the workgroup's 256 queries are one mask row; the steps
     // run over the sorted list of the key tiles it marks (a marked tile is
     // seen whole, apart from the causal diagonal and the ragged last tile)
@@ -730,14 +721,6 @@ void fa_bwd_dq_kernel(BwdParams p) {
         n_kt = *list_len;
     }
 
-    bf16x8 qreg[KK], greg[KK];
-    load_frag<D>(qreg, (const __bf16*)p.q + qoff, p.q_sn, q, Nq, hi);
-    load_frag<D>(greg, (const __bf16*)p.dout + qoff, p.q_sn, q, Nq, hi);
-    float lse2 = 0.f, dlt = 0.f;
-    if (q < Nq) {
-        lse2 = p.lse[(long long)bh * Nq + q] * kLog2e;
-        dlt = p.delta[(long long)bh * Nq + q];
-    }
 
     f32x16 acc[DB];
 #pragma unroll

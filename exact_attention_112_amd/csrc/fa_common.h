@@ -1,7 +1,8 @@
 // fa_common.h -- device primitives shared by the attention kernels of
 // libfa355 for gfx950 (AMD Instinct MI355X): vector types, LDS address
 // spaces, the workgroup -> (head, tile) map, the LDS swizzles, bf16 packing,
-// the cross-half reductions of a wave and the direct HBM -> LDS load.
+// the cross-half reductions of a wave, the direct HBM -> LDS load and the
+// list of a block-sparse mask row or column.
 #ifndef FA355_COMMON_H
 #define FA355_COMMON_H
 
@@ -156,6 +157,35 @@ __device__ __forceinline__ void issue_tile(unsigned long long tile, unsigned rb,
             load_lds16(rsrc, dst + j * RPL * DCH * 16, o, j * RPL * rb);
         }
     }
+}
+
+// Sorted list of the indices t < n whose entry(t) is nonzero (a block-sparse
+// mask row or column), built by one wave into LDS; returns the count.  Bits
+// 12-15 of entry(t) are kept in the stored entry (t < 4096).  A round covers
+// 256 indices: lane i tests 4i .. 4i+3, so the mask reads of a round are in
+// flight together and a list of up to 256 entries costs one memory latency.
+// An entry's position is the number of marked indices in the lower lanes
+// (ballot + mbcnt per slot) plus those before it in its own lane.
+template <typename F>
+__device__ __forceinline__ int build_list(unsigned short* list, int n, int lane, F entry) {
+    int count = 0;
+    for (int base = 0; base < n; base += 256) {
+        const int t0 = base + 4 * lane;
+        unsigned e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = t0 + i < n ? entry(t0 + i) : 0u;
+        int pos = count;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const unsigned long long bal = __builtin_amdgcn_ballot_w64(e[i] != 0u);
+            pos += (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+            count += __builtin_popcountll(bal);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (e[i] != 0u) list[pos++] = (unsigned short)((unsigned)(t0 + i) | (e[i] & 0xF000u));
+    }
+    return count;
 }
 
 }  // namespace fa355

@@ -502,6 +502,19 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         hi_key = min(Nk - 1, wr >= 0 ? q + wr : big);
         if (CAUSAL) hi_key = min(hi_key, q);
     }
+    // ---- Q fragment (B operand of S^T = K Q^T): lane holds Q[q][16kk + 8hi .. +7]
+    // (loaded before the block-sparse list is built, so the two latencies overlap)
+    bf16x8 qreg[KK];
+    {
+        const bool ok = q < Nq;
+        const __bf16* qrow = qbase + (long long)(ok ? q : 0) * p.q_sn + hi * 8;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            u32x4 x = ok ? *(const u32x4*)(qrow + kk * 16) : (u32x4){0u, 0u, 0u, 0u};
+            qreg[kk] = __builtin_bit_cast(bf16x8, x);
+        }
+    }
+
     // Block-sparse: the workgroup walks the sorted list of its unmasked-off
     // tiles; "tile" v below is then list entry v.  The tiles a wave or the
     // whole workgroup sees in full are a prefix of the list (the list is
@@ -509,16 +522,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     if constexpr (SPARSE) {
         const unsigned char* mrow = p.block_mask + ((long long)bh * p.n_qb + qt) * p.n_kb;
         if (wave == 0) {
-            int count = 0;
-            for (int base = 0; base < n_kt; base += 64) {
-                const int t = base + lane;
-                const bool on = t < n_kt && mrow[t] != 0;
-                const unsigned long long bal = __builtin_amdgcn_ballot_w64(on);
-                const int pos = count + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
-                                                                      __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
-                if (on) tile_list[pos] = (unsigned short)t;
-                count += __builtin_popcountll(bal);
-            }
+            const int count = build_list(tile_list, n_kt, lane, [&](int t) { return mrow[t] != 0 ? 1u : 0u; });
             if (lane == 0) *list_len = count;
         }
         __syncthreads();
@@ -537,18 +541,6 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         hi_key = CAUSAL ? min(Nk - 1, q) : Nk - 1;
     }
 #define FA_TILE(v) (SPARSE ? (int)tile_list[(v)] : (v))
-
-    // ---- Q fragment (B operand of S^T = K Q^T): lane holds Q[q][16kk + 8hi .. +7]
-    bf16x8 qreg[KK];
-    {
-        const bool ok = q < Nq;
-        const __bf16* qrow = qbase + (long long)(ok ? q : 0) * p.q_sn + hi * 8;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            u32x4 x = ok ? *(const u32x4*)(qrow + kk * 16) : (u32x4){0u, 0u, 0u, 0u};
-            qreg[kk] = __builtin_bit_cast(bf16x8, x);
-        }
-    }
 
     // ---- direct HBM -> LDS staging (buffer_load ... lds, 16 bytes a lane).
     // Each wave instruction writes 64 consecutive 16-byte LDS chunks: RPW
