@@ -252,7 +252,7 @@ template <int D, bool MASK, bool UPPER>
 __device__ __forceinline__ void dkdv_step(f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], const bf16x8 (&kreg)[D / 16],
                                           const lds_char* qt, const lds_char* gt, const lds_char* vb,
                                           const float* __restrict__ st, DkdvOffsets o, int hi, float sl2, int vlo,
-                                          int vhi) {
+                                          int vhi, bool masked) {
     constexpr int KK = D / 16, DB = D / 32, NT = 2 * DB, RB = D * 2;
     // the offsets pass through an empty asm statement: the compiler then
     // forms each read's address next to the read, every step, instead of
@@ -316,17 +316,25 @@ __device__ __forceinline__ void dkdv_step(f32x16 (&dk)[D / 32], f32x16 (&dv)[D /
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gf[kk % (GB + 1)], vf[kk % (GB + 1)], kk == 0 ? f32x16{} : dp,
                                                      0, 0, 0);
         if (kk >= 1) {
+            const int e0 = 16 * (kk - 1) / (KK - 1), e1 = 16 * kk / (KK - 1);
 #pragma unroll
-            for (int e = 16 * (kk - 1) / (KK - 1); e < 16 * kk / (KK - 1); ++e) {
+            for (int e = e0; e < e1; ++e) {
                 const int g = e >> 2;
                 if ((e & 3) == 0 && g + 1 < 4) l4[(g + 1) & 1] = lds_f4(st + (g + 1) * 8 + hi * 4);
                 const float4 l = l4[g & 1];
                 const float lv = (e & 3) == 0 ? l.x : (e & 3) == 1 ? l.y : (e & 3) == 2 ? l.z : l.w;
-                float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sl2, -lv));
-                if (!vis(e)) pe = 0.f;
-                s[e] = pe;
-                if (e & 1) pkp[e >> 1] = pack_bf16x2(s[e - 1], pe);
+                s[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sl2, -lv));
             }
+            // the mask only on the tiles that cross an edge (a wave-uniform
+            // branch: the other tiles skip its compares and selects)
+            if (MASK && masked) {
+#pragma unroll
+                for (int e = e0; e < e1; ++e)
+                    if (!vis(e)) s[e] = 0.f;
+            }
+#pragma unroll
+            for (int e = e0; e < e1; ++e)
+                if (e & 1) pkp[e >> 1] = pack_bf16x2(s[e - 1], s[e]);
         }
         if (kk == KK - 1) d4[0] = lds_f4(st + 32 + 0 * 8 + hi * 4);
         __builtin_amdgcn_sched_barrier(0);
@@ -604,14 +612,14 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             masked = masked || (p.wl >= 0 && i0 + BQ - 1 - p.wl > kw0) || (p.wr >= 0 && i0 + p.wr < kw0 + 31);
         if constexpr (CAUSAL || BAND) {
             // element bounds of dkdv_step (the lane's query offset less hi*4),
-            // open on the tiles that cross no edge
+            // used only on the tiles that cross an edge
             const int base = key - i0 - hi * 4;
-            int vlo = CAUSAL && masked ? base : -(1 << 30), vhi = 1 << 30;
-            if (BAND && masked && p.wr >= 0) vlo = max(vlo, (int)max((long long)base - p.wr, -(1LL << 30)));
-            if (BAND && masked && p.wl >= 0) vhi = (int)min((long long)base + p.wl, 1LL << 30);
-            dkdv_step<D, true, BAND>(dk, dv, kreg, qt, gt, vblk, st, offs, hi, sl2, vlo, vhi);
+            int vlo = CAUSAL ? base : -(1 << 30), vhi = 1 << 30;
+            if (BAND && p.wr >= 0) vlo = max(vlo, (int)max((long long)base - p.wr, -(1LL << 30)));
+            if (BAND && p.wl >= 0) vhi = (int)min((long long)base + p.wl, 1LL << 30);
+            dkdv_step<D, true, BAND>(dk, dv, kreg, qt, gt, vblk, st, offs, hi, sl2, vlo, vhi, masked);
         } else {
-            dkdv_step<D, false, false>(dk, dv, kreg, qt, gt, vblk, st, offs, hi, sl2, 0, 0);
+            dkdv_step<D, false, false>(dk, dv, kreg, qt, gt, vblk, st, offs, hi, sl2, 0, 0, false);
         }
     }
 #undef FA_ISSUE_QG
