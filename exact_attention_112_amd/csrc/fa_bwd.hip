@@ -288,6 +288,12 @@ __device__ __forceinline__ void dkdv_step(f32x16 (&dk)[D / 32], f32x16 (&dv)[D /
     bf16x8 qf[QA + 1], gf[GB + 1], vf[GB + 1], tf[TC + 1];
     float4 l4[2], d4[2];
 
+    // The wave raises its issue priority (s_setprio 1) over chains A and B
+    // (the scores and the exponentials) and drops it for C and D, so the two
+    // waves of a SIMD tend to take turns; measured 0.4 % faster on the
+    // B4 H32 N8192 backward, 1.0 % on the causal and 2.5 % on the band one,
+    // while priority over the dQ kernel's step made the first slower.
+    __builtin_amdgcn_s_setprio(1);
     // A: S chain; Q reads QA MFMAs ahead, then the first dO / V reads for B
 #pragma unroll
     for (int i = 0; i < QA; ++i) qf[i] = qread(i);
@@ -339,6 +345,7 @@ __device__ __forceinline__ void dkdv_step(f32x16 (&dk)[D / 32], f32x16 (&dv)[D /
         if (kk == KK - 1) d4[0] = lds_f4(st + 32 + 0 * 8 + hi * 4);
         __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     // C: dV chain, transposed reads TC MFMAs ahead (read n = 0 .. 2NT-1:
     // dO^T for C, then Q^T for D, into tf[n % (TC+1)]); dS over groups
     // 1 .. NT-1
