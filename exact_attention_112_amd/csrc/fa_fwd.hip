@@ -422,6 +422,76 @@ struct Bf16Cfg {
     static_assert(TILE_CH % (64 * NW) == 0, "tile must split evenly over the waves");
 };
 
+// O of a wave's 32 rows written to HBM, each lane's own row scaled by its
+// 1/l (`inv`).  As accumulated, the lanes of row c (col c, hi 0 and 1) hold
+// its 16-byte pieces 2m + hi (m = 4 db + g): one store per register set wrote
+// 32 bytes into each of 32 rows.  v_permlane16_swap trades the pieces of two
+// adjacent m, 2m' and 2m' + 1, between the lanes of rows c and c + 16
+// (c < 16): afterwards the first register set of the four lanes of cols c and
+// c + 16 holds pieces 4m' .. 4m' + 3 of row c, the second those of row c + 16,
+// so every store writes 64 contiguous, aligned bytes into each of 16 rows
+// (half the write requests).  Every lane must be active at the swaps; rows at
+// or past n_rows are not stored.
+__device__ __forceinline__ void swap_rows16(unsigned& a, unsigned& b) {
+    // lanes 16..31 and 48..63 of a trade with lanes 0..15 and 32..47 of b
+    // (the s_nop covers the VALU-write -> permlane-read hazard)
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+// SITE: each kernel instantiates its own copy (with one copy inlined into
+// both kernels, the compiler allocated the ordinary kernel's registers
+// differently and it spilled).
+template <int D, bool OUT_BF16, int SITE>
+__device__ __forceinline__ void store_o_rows(f32x16 (&oacc)[D / 32], float inv, char* o_row0, long long row_elems,
+                                             int n_rows, int col, int hi) {
+    constexpr int DB = D / 32, ES = OUT_BF16 ? 2 : 4;
+    const int sel = col >> 4;
+    const int r = col & 15;
+    const bool ok0 = r < n_rows, ok1 = r + 16 < n_rows;
+    char* const p0 = o_row0 + (long long)r * row_elems * ES;   // row r
+    char* const p1 = p0 + 16LL * row_elems * ES;                // row r + 16
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        oacc[db] *= inv;   // in place: the accumulator is dead after the store
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+            // elements 8 gp .. 8 gp + 3: piece 2m' + hi (g = 2 gp) of this lane's row;
+            // 8 gp + 4 .. + 7: piece 2m' + 2 + hi (g = 2 gp + 1)
+            const int e0 = 8 * gp;
+            // swapped: elements e0.. hold row r, e0 + 4.. row r + 16, piece
+            // 8 db + 4 gp + 2 sel + hi of that row
+            const int dd = db * 32 + gp * 16 + sel * 8 + hi * 4;
+            if constexpr (OUT_BF16) {
+                unsigned x0 = pack_bf16x2(oacc[db][e0], oacc[db][e0 + 1]);
+                unsigned x1 = pack_bf16x2(oacc[db][e0 + 2], oacc[db][e0 + 3]);
+                unsigned y0 = pack_bf16x2(oacc[db][e0 + 4], oacc[db][e0 + 5]);
+                unsigned y1 = pack_bf16x2(oacc[db][e0 + 6], oacc[db][e0 + 7]);
+                swap_rows16(x0, y0);
+                swap_rows16(x1, y1);
+                if (ok0) *(u32x2*)(p0 + dd * 2) = (u32x2){x0, x1};
+                if (ok1) *(u32x2*)(p1 + dd * 2) = (u32x2){y0, y1};
+            } else {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    // (through a float: a bit cast of a vector element itself reads element 0)
+                    const float fx = oacc[db][e0 + w], fy = oacc[db][e0 + 4 + w];
+                    unsigned x = __builtin_bit_cast(unsigned, fx);
+                    unsigned y = __builtin_bit_cast(unsigned, fy);
+                    swap_rows16(x, y);
+                    oacc[db][e0 + w] = __builtin_bit_cast(float, x);
+                    oacc[db][e0 + 4 + w] = __builtin_bit_cast(float, y);
+                }
+                if (ok0)
+                    *(float4*)(p0 + dd * 4) =
+                        make_float4(oacc[db][e0], oacc[db][e0 + 1], oacc[db][e0 + 2], oacc[db][e0 + 3]);
+                if (ok1)
+                    *(float4*)(p1 + dd * 4) =
+                        make_float4(oacc[db][e0 + 4], oacc[db][e0 + 5], oacc[db][e0 + 6], oacc[db][e0 + 7]);
+            }
+        }
+    }
+}
+
 // MODE kBand: keys outside the band i-wl .. i+wr are masked and the tiles
 // outside the workgroup's band are never loaded.  MODE kSparse: the key
 // tiles a block mask marks off for the workgroup's 256 queries are never
@@ -696,25 +766,14 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     const float dl_tot = pair_sum(st.dl);
     // the lane's half, recomputed (mbcnt) rather than kept live through the loops
     const int hi_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5;
-    if (q < Nq) {
+    {
         // (band: a row that saw no key has l = 0 and gets O = 0, LSE = -inf)
         const float inv = (!SAFE || l_tot > 0.f) ? 1.0f / (l_tot + dl_tot) : 0.f;
-        char* obase = (char*)p.o;
-        const long long orow = (long long)b * p.q_sb + (long long)h * p.q_sh + (long long)q * p.q_sn;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int dd = db * 32 + g * 8 + hi_e * 4;
-                const float o0 = st.oacc[db][4 * g + 0] * inv, o1 = st.oacc[db][4 * g + 1] * inv;
-                const float o2 = st.oacc[db][4 * g + 2] * inv, o3 = st.oacc[db][4 * g + 3] * inv;
-                if constexpr (OUT_BF16) {
-                    u32x2 w = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-                    *(u32x2*)(obase + (orow + dd) * 2) = w;
-                } else {
-                    *(float4*)(obase + (orow + dd) * 4) = make_float4(o0, o1, o2, o3);
-                }
-            }
+        const long long orow0 = (long long)b * p.q_sb + (long long)h * p.q_sh + (long long)q_w0 * p.q_sn;
+        store_o_rows<D, OUT_BF16, 0>(st.oacc, inv, (char*)p.o + orow0 * (OUT_BF16 ? 2 : 4), p.q_sn, Nq - q_w0,
+                                  col, hi_e);
+    }
+    if (q < Nq) {
         if (p.lse && hi_e == 0)
             p.lse[(long long)bh * Nq + q] = (!SAFE || l_tot > 0.f) ? (st.m + __builtin_amdgcn_logf(l_tot)) * kLn2
                                                                    : -INFINITY;
@@ -833,28 +892,17 @@ void fa_fwd_bf16_persist(FwdParams p, int n_items) {
         const float l_tot = pair_sum(st.l0 + st.l1);
         const float dl_tot = pair_sum(st.dl);
         const int hi_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5;
-        const int q = it.q0 + my_row;
-        if (q < Nq) {
+        const int q_w0 = it.q0 + wave * 32;
+        const int q = q_w0 + col;
+        {
             const float inv = 1.0f / (l_tot + dl_tot);
             const int b = it.bh / p.H, h = it.bh - b * p.H;
-            char* obase = (char*)p.o;
-            const long long orow = (long long)b * p.q_sb + (long long)h * p.q_sh + (long long)q * p.q_sn;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int dd = db * 32 + g * 8 + hi_e * 4;
-                    const float o0 = st.oacc[db][4 * g + 0] * inv, o1 = st.oacc[db][4 * g + 1] * inv;
-                    const float o2 = st.oacc[db][4 * g + 2] * inv, o3 = st.oacc[db][4 * g + 3] * inv;
-                    if constexpr (OUT_BF16) {
-                        u32x2 w = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-                        *(u32x2*)(obase + (orow + dd) * 2) = w;
-                    } else {
-                        *(float4*)(obase + (orow + dd) * 4) = make_float4(o0, o1, o2, o3);
-                    }
-                }
-            if (p.lse && hi_e == 0) p.lse[(long long)it.bh * Nq + q] = (st.m + __builtin_amdgcn_logf(l_tot)) * kLn2;
+            const long long orow0 = (long long)b * p.q_sb + (long long)h * p.q_sh + (long long)q_w0 * p.q_sn;
+            store_o_rows<D, OUT_BF16, 1>(st.oacc, inv, (char*)p.o + orow0 * (OUT_BF16 ? 2 : 4), p.q_sn, Nq - q_w0,
+                                      col, hi_e);
         }
+        if (q < Nq && p.lse && hi_e == 0)
+            p.lse[(long long)it.bh * Nq + q] = (st.m + __builtin_amdgcn_logf(l_tot)) * kLn2;
     };
 
     int item = __builtin_amdgcn_workgroup_id_x();
@@ -921,16 +969,21 @@ void fa_fwd_bf16_persist(FwdParams p, int n_items) {
         // j = n_kt - 1: P of the last tile; the next query tile's Q and its
         // K tile 0 landed at this top
         FA_TOP(j);
+        float m_next = 0.f;
         if (!has_nxt) {
             wave_step_serial<D, false, false>(st, sb, qreg, nullptr, FA_V_STAGE(j), 0, 0, Nk, sl2, col, hi, tr_row,
                                               tr_dd);
-            store_out(cur);
-            break;
+        } else {
+            load_q();
+            m_next = wave_step_sw<D, true>(st, sb, sa, qreg, (const u32x4*)FA_K_STAGE(0), FA_V_STAGE(j), sl2, col,
+                                           hi, tr_row, tr_dd);
         }
-        load_q();
-        const float m_next = wave_step_sw<D, true>(st, sb, sa, qreg, (const u32x4*)FA_K_STAGE(0), FA_V_STAGE(j),
-                                                   sl2, col, hi, tr_row, tr_dd);
         store_out(cur);
+        if (!has_nxt) break;
+        // the Q fragments again, so that they hold no registers during the
+        // stores (the empty asm keeps the compiler from reusing the first read)
+        asm volatile("" ::: "memory");
+        load_q();
         reset(m_next);
         item = nxt;
         cur = next;
