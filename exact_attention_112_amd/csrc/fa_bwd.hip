@@ -145,20 +145,6 @@ __device__ __forceinline__ void load_frag(bf16x8 (&f)[D / 16], const __bf16* bas
     }
 }
 
-// Store a d x 32 accumulator (transposed: lane column = the row of the
-// output, registers = d) times `mul` as fp32 rows of the output.
-template <int D>
-__device__ __forceinline__ void store_rows_f32(float* out_row, const f32x16 (&acc)[D / 32], float mul, int hi) {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int dd = db * 32 + g * 8 + hi * 4;
-            *(float4*)(out_row + dd) = make_float4(acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul,
-                                                   acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul);
-        }
-}
-
 // ---------------------------------------------------------------------------
 // 1. D_i = dO_i . O_i, one row per D/8 threads (8 elements each).
 template <int D, bool O_BF16>
@@ -757,10 +743,9 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     }
 #undef FA_ISSUE_QG
 
-    if (key < Nk) {
-        store_rows_f32<D>(p.dk + koff + (long long)key * p.k_sn, dk, p.scale, hi);
-        store_rows_f32<D>(p.dv + koff + (long long)key * p.k_sn, dv, 1.0f, hi);
-    }
+    store_acc_rows<D, false, 0>(dk, p.scale, (char*)(p.dk + koff + (long long)kw0 * p.k_sn), p.k_sn, Nk - kw0, col,
+                                hi);
+    store_acc_rows<D, false, 1>(dv, 1.0f, (char*)(p.dv + koff + (long long)kw0 * p.k_sn), p.k_sn, Nk - kw0, col, hi);
 }
 
 // ---------------------------------------------------------------------------
@@ -958,7 +943,8 @@ void fa_bwd_dq_kernel(BwdParams p) {
 #undef FA_ISSUE_KV
 #undef FA_STEP_TILE
 
-    if (q < Nq) store_rows_f32<D>(p.dq + qoff + (long long)q * p.q_sn, acc, p.scale, hi);
+    store_acc_rows<D, false, 2>(acc, p.scale, (char*)(p.dq + qoff + (long long)q_w0 * p.q_sn), p.q_sn, Nq - q_w0, col,
+                                hi);
 }
 
 }  // namespace fa355

@@ -188,6 +188,80 @@ __device__ __forceinline__ int build_list(unsigned short* list, int n, int lane,
     return count;
 }
 
+// A d x 32 accumulator of one wave (lane column = the output row, registers
+// = d: acc[db][r] is row col, element db*32 + (r/4)*8 + hi*4 + r%4) times
+// `mul`, written as rows of the output.  As accumulated, the lanes of row c
+// (col c, hi 0 and 1) hold its 16-byte pieces 2m + hi (m = 4 db + g, g =
+// r/4): one store per register set would write 32 bytes into each of 32
+// rows.  v_permlane16_swap trades the pieces of two adjacent m, 2m' and
+// 2m' + 1, between the lanes of rows c and c + 16 (c < 16): afterwards the
+// first register set of the four lanes of cols c and c + 16 holds pieces
+// 4m' .. 4m' + 3 of row c, the second those of row c + 16, so every store
+// writes 64 contiguous, aligned bytes into each of 16 rows (half the write
+// requests).  Every lane must be active; rows at or past n_rows are not
+// stored.  The accumulator is scaled and swapped in place (it is dead
+// afterwards).  row0 points at element 0 of the wave's first row; rows are
+// row_elems elements apart; OUT_BF16 rounds to bf16 (else fp32).
+// SITE: each call site instantiates its own copy (one copy inlined into two
+// kernels changed how the compiler allocated the other kernel's registers).
+__device__ __forceinline__ void swap_rows16(unsigned& a, unsigned& b) {
+    // lanes 16..31 and 48..63 of a trade with lanes 0..15 and 32..47 of b
+    // (the s_nop covers the VALU-write -> permlane-read hazard)
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+template <int D, bool OUT_BF16, int SITE>
+__device__ __forceinline__ void store_acc_rows(f32x16 (&acc)[D / 32], float mul, char* row0, long long row_elems,
+                                               int n_rows, int col, int hi) {
+    constexpr int DB = D / 32, ES = OUT_BF16 ? 2 : 4;
+    const int sel = col >> 4;
+    const int r = col & 15;
+    const bool ok0 = r < n_rows, ok1 = r + 16 < n_rows;
+    char* const p0 = row0 + (long long)r * row_elems * ES;   // row r
+    char* const p1 = p0 + 16LL * row_elems * ES;              // row r + 16
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        acc[db] *= mul;
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+            // elements 8 gp .. 8 gp + 3: piece 2m' + hi (g = 2 gp) of this
+            // lane's row; 8 gp + 4 .. + 7: piece 2m' + 2 + hi (g = 2 gp + 1).
+            // Swapped, elements e0.. hold row r and e0 + 4.. row r + 16, piece
+            // 8 db + 4 gp + 2 sel + hi of that row.
+            const int e0 = 8 * gp;
+            const int dd = db * 32 + gp * 16 + sel * 8 + hi * 4;
+            if constexpr (OUT_BF16) {
+                unsigned x0 = pack_bf16x2(acc[db][e0], acc[db][e0 + 1]);
+                unsigned x1 = pack_bf16x2(acc[db][e0 + 2], acc[db][e0 + 3]);
+                unsigned y0 = pack_bf16x2(acc[db][e0 + 4], acc[db][e0 + 5]);
+                unsigned y1 = pack_bf16x2(acc[db][e0 + 6], acc[db][e0 + 7]);
+                swap_rows16(x0, y0);
+                swap_rows16(x1, y1);
+                if (ok0) *(u32x2*)(p0 + dd * 2) = (u32x2){x0, x1};
+                if (ok1) *(u32x2*)(p1 + dd * 2) = (u32x2){y0, y1};
+            } else {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    // (through a float: a bit cast of a vector element itself
+                    // reads element 0)
+                    const float fx = acc[db][e0 + w], fy = acc[db][e0 + 4 + w];
+                    unsigned x = __builtin_bit_cast(unsigned, fx);
+                    unsigned y = __builtin_bit_cast(unsigned, fy);
+                    swap_rows16(x, y);
+                    acc[db][e0 + w] = __builtin_bit_cast(float, x);
+                    acc[db][e0 + 4 + w] = __builtin_bit_cast(float, y);
+                }
+                if (ok0)
+                    *(float4*)(p0 + dd * 4) =
+                        make_float4(acc[db][e0], acc[db][e0 + 1], acc[db][e0 + 2], acc[db][e0 + 3]);
+                if (ok1)
+                    *(float4*)(p1 + dd * 4) =
+                        make_float4(acc[db][e0 + 4], acc[db][e0 + 5], acc[db][e0 + 6], acc[db][e0 + 7]);
+            }
+        }
+    }
+}
+
 }  // namespace fa355
 
 #endif  // FA355_COMMON_H

@@ -422,76 +422,6 @@ struct Bf16Cfg {
     static_assert(TILE_CH % (64 * NW) == 0, "tile must split evenly over the waves");
 };
 
-// O of a wave's 32 rows written to HBM, each lane's own row scaled by its
-// 1/l (`inv`).  As accumulated, the lanes of row c (col c, hi 0 and 1) hold
-// its 16-byte pieces 2m + hi (m = 4 db + g): one store per register set wrote
-// 32 bytes into each of 32 rows.  v_permlane16_swap trades the pieces of two
-// adjacent m, 2m' and 2m' + 1, between the lanes of rows c and c + 16
-// (c < 16): afterwards the first register set of the four lanes of cols c and
-// c + 16 holds pieces 4m' .. 4m' + 3 of row c, the second those of row c + 16,
-// so every store writes 64 contiguous, aligned bytes into each of 16 rows
-// (half the write requests).  Every lane must be active at the swaps; rows at
-// or past n_rows are not stored.
-__device__ __forceinline__ void swap_rows16(unsigned& a, unsigned& b) {
-    // lanes 16..31 and 48..63 of a trade with lanes 0..15 and 32..47 of b
-    // (the s_nop covers the VALU-write -> permlane-read hazard)
-    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-
-// SITE: each kernel instantiates its own copy (with one copy inlined into
-// both kernels, the compiler allocated the ordinary kernel's registers
-// differently and it spilled).
-template <int D, bool OUT_BF16, int SITE>
-__device__ __forceinline__ void store_o_rows(f32x16 (&oacc)[D / 32], float inv, char* o_row0, long long row_elems,
-                                             int n_rows, int col, int hi) {
-    constexpr int DB = D / 32, ES = OUT_BF16 ? 2 : 4;
-    const int sel = col >> 4;
-    const int r = col & 15;
-    const bool ok0 = r < n_rows, ok1 = r + 16 < n_rows;
-    char* const p0 = o_row0 + (long long)r * row_elems * ES;   // row r
-    char* const p1 = p0 + 16LL * row_elems * ES;                // row r + 16
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        oacc[db] *= inv;   // in place: the accumulator is dead after the store
-#pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
-            // elements 8 gp .. 8 gp + 3: piece 2m' + hi (g = 2 gp) of this lane's row;
-            // 8 gp + 4 .. + 7: piece 2m' + 2 + hi (g = 2 gp + 1)
-            const int e0 = 8 * gp;
-            // swapped: elements e0.. hold row r, e0 + 4.. row r + 16, piece
-            // 8 db + 4 gp + 2 sel + hi of that row
-            const int dd = db * 32 + gp * 16 + sel * 8 + hi * 4;
-            if constexpr (OUT_BF16) {
-                unsigned x0 = pack_bf16x2(oacc[db][e0], oacc[db][e0 + 1]);
-                unsigned x1 = pack_bf16x2(oacc[db][e0 + 2], oacc[db][e0 + 3]);
-                unsigned y0 = pack_bf16x2(oacc[db][e0 + 4], oacc[db][e0 + 5]);
-                unsigned y1 = pack_bf16x2(oacc[db][e0 + 6], oacc[db][e0 + 7]);
-                swap_rows16(x0, y0);
-                swap_rows16(x1, y1);
-                if (ok0) *(u32x2*)(p0 + dd * 2) = (u32x2){x0, x1};
-                if (ok1) *(u32x2*)(p1 + dd * 2) = (u32x2){y0, y1};
-            } else {
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    // (through a float: a bit cast of a vector element itself reads element 0)
-                    const float fx = oacc[db][e0 + w], fy = oacc[db][e0 + 4 + w];
-                    unsigned x = __builtin_bit_cast(unsigned, fx);
-                    unsigned y = __builtin_bit_cast(unsigned, fy);
-                    swap_rows16(x, y);
-                    oacc[db][e0 + w] = __builtin_bit_cast(float, x);
-                    oacc[db][e0 + 4 + w] = __builtin_bit_cast(float, y);
-                }
-                if (ok0)
-                    *(float4*)(p0 + dd * 4) =
-                        make_float4(oacc[db][e0], oacc[db][e0 + 1], oacc[db][e0 + 2], oacc[db][e0 + 3]);
-                if (ok1)
-                    *(float4*)(p1 + dd * 4) =
-                        make_float4(oacc[db][e0 + 4], oacc[db][e0 + 5], oacc[db][e0 + 6], oacc[db][e0 + 7]);
-            }
-        }
-    }
-}
-
 // MODE kBand: keys outside the band i-wl .. i+wr are masked and the tiles
 // outside the workgroup's band are never loaded.  MODE kSparse: the key
 // tiles a block mask marks off for the workgroup's 256 queries are never
@@ -770,7 +700,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         // (band: a row that saw no key has l = 0 and gets O = 0, LSE = -inf)
         const float inv = (!SAFE || l_tot > 0.f) ? 1.0f / (l_tot + dl_tot) : 0.f;
         const long long orow0 = (long long)b * p.q_sb + (long long)h * p.q_sh + (long long)q_w0 * p.q_sn;
-        store_o_rows<D, OUT_BF16, 0>(st.oacc, inv, (char*)p.o + orow0 * (OUT_BF16 ? 2 : 4), p.q_sn, Nq - q_w0,
+        store_acc_rows<D, OUT_BF16, 0>(st.oacc, inv, (char*)p.o + orow0 * (OUT_BF16 ? 2 : 4), p.q_sn, Nq - q_w0,
                                   col, hi_e);
     }
     if (q < Nq) {
@@ -898,7 +828,7 @@ void fa_fwd_bf16_persist(FwdParams p, int n_items) {
             const float inv = 1.0f / (l_tot + dl_tot);
             const int b = it.bh / p.H, h = it.bh - b * p.H;
             const long long orow0 = (long long)b * p.q_sb + (long long)h * p.q_sh + (long long)q_w0 * p.q_sn;
-            store_o_rows<D, OUT_BF16, 1>(st.oacc, inv, (char*)p.o + orow0 * (OUT_BF16 ? 2 : 4), p.q_sn, Nq - q_w0,
+            store_acc_rows<D, OUT_BF16, 1>(st.oacc, inv, (char*)p.o + orow0 * (OUT_BF16 ? 2 : 4), p.q_sn, Nq - q_w0,
                                       col, hi_e);
         }
         if (q < Nq && p.lse && hi_e == 0)
@@ -922,6 +852,9 @@ void fa_fwd_bf16_persist(FwdParams p, int n_items) {
     st.xl = -INFINITY;
     reset(tile_max_scaled(sa, sl2, st.xl));
 
+    // every wave's wait for its own tile loads sits at the end of the step
+    // before a top (the first top of a query tile: after the O stores)
+#define FA_WAIT_LOADS() asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
     for (;;) {
         const int nxt = item + G;
         const bool has_nxt = nxt < n_items;
@@ -933,7 +866,6 @@ void fa_fwd_bf16_persist(FwdParams p, int n_items) {
         // then computes P_j, O += P_j V_j and the scores of tile j+1.
 #define FA_TOP(j)                                                                  \
     do {                                                                           \
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                           \
         __syncthreads();                                                           \
         if ((j) + 2 < n_kt) FA_ISSUE_K(k_cur, (j) + 2);                            \
         else if (has_nxt) FA_ISSUE_K(k_nxt, (j) + 2 - n_kt);                       \
@@ -944,7 +876,6 @@ void fa_fwd_bf16_persist(FwdParams p, int n_items) {
         // (n_kt is even, so inside the loop every tile to load is this query tile's)
 #define FA_TOP_IN(j)                                      \
     do {                                                  \
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  \
         __syncthreads();                                  \
         FA_ISSUE_K(k_cur, (j) + 2);                       \
         FA_ISSUE_V(k_cur, (j) + 1);                       \
@@ -954,9 +885,11 @@ void fa_fwd_bf16_persist(FwdParams p, int n_items) {
             FA_TOP_IN(j);
             wave_step_sw<D>(st, sa, sb, qreg, (const u32x4*)FA_K_STAGE(j + 1), FA_V_STAGE(j), sl2, col, hi,
                             tr_row, tr_dd);
+            FA_WAIT_LOADS();
             FA_TOP_IN(j + 1);
             wave_step_sw<D>(st, sb, sa, qreg, (const u32x4*)FA_K_STAGE(j + 2), FA_V_STAGE(j + 1), sl2, col, hi,
                             tr_row, tr_dd);
+            FA_WAIT_LOADS();
         }
 #undef FA_TOP_IN
         // j = n_kt - 2: P_j and the scores of the last tile (the Q loads
@@ -965,6 +898,7 @@ void fa_fwd_bf16_persist(FwdParams p, int n_items) {
         FA_TOP(j);
         wave_step_sw<D>(st, sa, sb, qreg, (const u32x4*)FA_K_STAGE(j + 1), FA_V_STAGE(j), sl2, col, hi, tr_row,
                         tr_dd);
+        FA_WAIT_LOADS();
         ++j;
         // j = n_kt - 1: P of the last tile; the next query tile's Q and its
         // K tile 0 landed at this top
@@ -980,6 +914,12 @@ void fa_fwd_bf16_persist(FwdParams p, int n_items) {
         }
         store_out(cur);
         if (!has_nxt) break;
+        // the next query tile's first top needs K tile 1 and V tile 0, whose
+        // loads were issued before this wave's O stores: vector memory
+        // counts return in issue order, so after a full tile (D/8 stores)
+        // the wait lets the stores stay in flight
+        if (cur.q0 + wave * 32 + 32 <= Nq) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D / 8) : "memory");
+        else FA_WAIT_LOADS();
         // the Q fragments again, so that they hold no registers during the
         // stores (the empty asm keeps the compiler from reusing the first read)
         asm volatile("" ::: "memory");
@@ -995,6 +935,7 @@ void fa_fwd_bf16_persist(FwdParams p, int n_items) {
 #undef FA_ISSUE_K
 #undef FA_ISSUE_V
 #undef FA_ISSUE_Q
+#undef FA_WAIT_LOADS
 }
 
 // ---------------------------------------------------------------------------
