@@ -276,11 +276,12 @@ __device__ __forceinline__ float wave_step_sw(RowState<D>& st, const f32x16 (&s_
     constexpr int DCH = D / 8, DB = D / 32;
     constexpr int NA = 2 * (D / 16);      // score MFMAs
     constexpr int NB = 4 * DB;            // P V MFMAs
-    // exponentials (32 per lane and tile), element by element: EA of them
-    // spread evenly over the NA groups of phase A, the rest over the first GB
-    // groups of phase B, each before the P V MFMA that needs it (d = 128:
-    // 22 + 10, one or two per score MFMA and one per P V MFMA, so that no
-    // group's vector work exceeds what the other wave's MFMA hides)
+    // exponentials (32 per lane and tile), element by element: EA of them in
+    // phase A (the first EP before its first MFMA, the others spread evenly
+    // over its NA groups), the rest over the first GB groups of phase B, each
+    // before the P V MFMA that needs it (d = 128: 6 + 16 + 10, about one per
+    // score MFMA and one per P V MFMA, so that no group's vector work exceeds
+    // what the other wave's MFMA hides)
     constexpr int EA = D == 128 ? 22 : 32;
     constexpr int GB = D == 128 ? 10 : 1;
     constexpr int CPS = NB == 16 ? 1 : 2; // max chunks per P V MFMA
@@ -325,6 +326,14 @@ __device__ __forceinline__ float wave_step_sw(RowState<D>& st, const f32x16 (&s_
     // priorities; priority only over phase A, or to the end of phase B,
     // gained less, and around each MFMA alone it lost 1 %)
     __builtin_amdgcn_s_setprio(1);
+    // EP of phase A's exponentials go before its first MFMA: they need only
+    // this tile's scores (in registers), so they fill the wait for the first
+    // K fragments after the barrier (0.4-0.65 % faster at B4 H32 N8192 d128
+    // than none; 2, 4, 5 or 8 gained as much or less)
+    constexpr int EP = 6;
+#pragma unroll
+    for (int e = 0; e < EP; ++e) elem(e);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
         if (i + 3 < NA) kf[(i + 3) & 3] = kread(i + 3);
@@ -333,7 +342,7 @@ __device__ __forceinline__ float wave_step_sw(RowState<D>& st, const f32x16 (&s_
         s_nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], qreg[i >> 1], i < 2 ? f32x16{} : s_nxt[kb],
                                                             0, 0, 0);
 #pragma unroll
-        for (int e = (EA * i) / NA; e < (EA * (i + 1)) / NA; ++e) elem(e);
+        for (int e = EP + ((EA - EP) * i) / NA; e < EP + ((EA - EP) * (i + 1)) / NA; ++e) elem(e);
         __builtin_amdgcn_sched_barrier(0);
     }
     // phase B
