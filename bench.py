@@ -12,8 +12,9 @@ throughput in TFLOP/s (4*B*H*Nq*Nk*d, halved for causal) and:
   (2.5 PFLOP/s), timed live with HIP events on the stream the kernel runs on;
   ``traffic`` is the HBM bytes per launch from the committed rocprofv3 counter
   summary, or null when the kernel source changed since it was taken;
-* latency_ms: mean, median, min and max of the per-launch times (HIP events
-  around each launch), and the TFLOP/s at the median;
+* latency_ms: mean, median, min and max of the per-launch times (a second
+  pass of as many launches, with a HIP event between consecutive launches),
+  and the TFLOP/s at the median;
 * counters: the matrix-core busy fraction, vector-ALU busy fraction, LDS bank
   conflicts and HBM rate from the committed rocprofv3 counter summary of the
   current kernel source (null otherwise);
@@ -455,10 +456,12 @@ def bench_attention(args, w, steps: int, warmup: int, with_cpu: bool, min_warmup
     backward) pass on workload ``w`` after ``warmup`` untimed calls; returns
     the JSON record (None on a non-finite output).  With ``min_warmup_s`` the
     warmup continues past ``warmup`` calls until that much time has passed
-    (short kernels: the GPU clock ramps up over tens of milliseconds).  Each
-    launch is bracketed by HIP events on the stream the kernels run on;
-    ``ms_per_step`` is the mean over the timed launches (back to back, no
-    cache flush)."""
+    (short kernels: the GPU clock ramps up over tens of milliseconds).  The
+    timed launches run back to back (no cache flush) between two HIP events
+    on the stream the kernels run on; ``ms_per_step`` is their mean.  A
+    second pass of as many launches, with an event between consecutive
+    launches, gives the per-launch latencies (an event between launches adds
+    a few microseconds to each, which matters only for short kernels)."""
     import numpy as np
     import torch
     import exact_attention_112_amd as fa
@@ -513,18 +516,25 @@ def bench_attention(args, w, steps: int, warmup: int, with_cpu: bool, min_warmup
                 step()
             torch.cuda.synchronize()
     stream = torch.cuda.current_stream()        # the stream fa.fwd / fa.bwd launch on
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     print(f"bench: timing {steps} steps", file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # per-launch latencies: a second pass with an event between launches
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record(stream)
     for i in range(steps):
         step()
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    ms = ev[0].elapsed_time(ev[steps]) / steps
     srt = sorted(per)
-    latency = {"mean": round(ms, 4), "median": round(srt[len(srt) // 2] if len(srt) % 2 else
+    latency = {"mean": round(sum(per) / steps, 4), "median": round(srt[len(srt) // 2] if len(srt) % 2 else
                                                      0.5 * (srt[len(srt) // 2 - 1] + srt[len(srt) // 2]), 4),
                "min": round(srt[0], 4), "max": round(srt[-1], 4)}
     bwd = args.which == "bwd"
